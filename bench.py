@@ -1,0 +1,250 @@
+"""Benchmark of the fused look-ahead layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen3_8b_16k]
+
+Workload: the Qwen3-8B-shaped layer (batch 128, 32 query / 8 KV heads,
+head_dim 128, 16K context, K = 128 resident 16-token blocks, cap 0.05, bf16),
+synthetic seeded inputs.  One step = one look-ahead layer step for the whole
+batch: attention of the normal and draft rows over the resident sets, the
+draft summary scan, top-K and capped eviction (one fused kernel), with the
+queries drifting AR(1) from step to step and the resident sets carried.  The
+prefetch of the admitted blocks crosses the host link and is timed in its own
+leg (`pcie`), never in `value`.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL = "layer_step_bf16_kernel"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "layer_step_qwen3_8b_16k_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, ctx: np.ndarray) -> dict:
+    """Bytes the fused step must move per launch (one layer, whole batch)."""
+    B, H, K, d, Hq = cfg.batch, cfg.n_kv_heads, cfg.k_resident, cfg.head_dim, cfg.n_q_heads
+    es = cfg.esize
+    S = cfg.block_size
+    nb = np.minimum(-(-ctx.astype(np.int64) // S), cfg.max_blocks(int(ctx.max())))
+    m = cfg.max_admit()
+    kv = B * H * K * 2 * S * d * es                       # resident records (keys + values)
+    summ = int(H * nb.sum()) * 2 * d * es                  # min/max rows of every block
+    q_out = 2 * (B * 2 * Hq * d * es)                      # queries read, outputs written
+    maps = B * H * (K * 4 * 2          # p2l read + write
+                    + K * 4 * 2        # last_sel read + write
+                    + K * 4            # l2p lookups of the top-K
+                    + 2 * m * 4        # l2p updates
+                    + K * 8            # top-K index + score written
+                    + K * 12 + 4)      # admission list + count written
+    return dict(kv=kv, summaries=summ, q_out=q_out, maps=maps,
+                total=kv + summ + q_out + maps + B * 4)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_kv_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(algo_total: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, ctx, records_host, qs_host, nunits: int):
+    """The fp64 oracle (as it stands) on a sample of units of the same step."""
+    import oracle
+    from sparse_kv_block_amd import gen
+    B, H = cfg.batch, cfg.n_kv_heads
+    units = np.arange(0, B * H, max(1, (B * H) // nunits), dtype=np.int32)[:nunits]
+    nb = cfg.max_blocks(int(ctx.max()))
+    rec = oracle.as_np(records_host)
+    summ = np.zeros((B, H, nb, 2, cfg.head_dim), dtype=rec.dtype)
+    nth = oracle.default_threads()
+    oracle.summarize(rec, ctx, cfg.block_size, summ=summ, units=units, nthreads=nth)
+    l2p, p2l, ls = [x.numpy().copy() for x in gen.random_state(cfg, ctx, nb, 77, stamp_max=1)]
+    q = oracle.as_np(qs_host)
+    used = min(nth, len(units))
+    t0 = time.perf_counter()
+    oracle.attention(q, rec, p2l, ctx, cfg.block_size, units=units, nthreads=nth)
+    sc = oracle.block_scores(q, summ, ctx, cfg.block_size, 1, units=units, nthreads=nth)
+    idx, _ = oracle.topk(sc, ctx, cfg.block_size, cfg.k_resident, units=units)
+    oracle.capped_evict(idx, 1, cfg.max_admit(), l2p, p2l, ls, units=units)
+    dt = time.perf_counter() - t0
+    frac = len(units) / (B * H)
+    return {"value": frac / dt, "unit": "layer-steps/s", "cores": used, "kind": "oracle",
+            "sample": f"{len(units)} of {B * H} (request, KV head) units of one layer step "
+                      f"(attention, scan, top-K, eviction) in {dt:.2f} s, scaled to the whole step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen3_8b_16k")
+    ap.add_argument("--cpu-units", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pcie", action="store_true")
+    ap.add_argument("--query-sets", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the look-ahead step has "
+              "no cross-GPU exchange, see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from sparse_kv_block_amd import gen, lib
+    from sparse_kv_block_amd.configs import CONFIGS
+    from sparse_kv_block_amd.pipeline import Layer
+
+    cfg = CONFIGS[args.config]
+    dev = "cuda"
+    ctx = gen.context_lengths(cfg)
+    nbmax = cfg.max_blocks(int(ctx.max()))
+    nq = args.query_sets
+    log(f"[bench] {cfg.name}: B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} d={cfg.head_dim} "
+        f"NBmax={nbmax} K={cfg.k_resident} m={cfg.max_admit()}")
+    qseq = gen.query_sequence(cfg, nq + 1, device=dev)
+    dirs = gen.planted_directions(cfg, qseq[1]) if cfg.planted else None
+    qs = [gen.step_queries(cfg, qseq, s) for s in range(1, nq + 1)]
+    t0 = time.perf_counter()
+    rec_dev = gen.records(cfg, ctx, nbmax, device=dev, planted_dir=dirs)
+    torch.cuda.synchronize()
+    log(f"[bench] generated {rec_dev.numel() * rec_dev.element_size() / 2**30:.1f} GiB of records "
+        f"in {time.perf_counter() - t0:.1f} s")
+    layer = Layer(cfg, ctx, nbmax, device=dev)
+    layer.summarize(rec_dev)
+    rec_host = torch.empty(rec_dev.shape, dtype=rec_dev.dtype, pin_memory=True)
+    rec_host.copy_(rec_dev)
+    del rec_dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    layer.cold_fill(qs[0], rec_host)
+    torch.cuda.synchronize()
+    log("[bench] cold fill done")
+
+    stream = torch.cuda.current_stream()
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        layer.step(qs[(step - 1) % nq], step)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step += 1
+        starts[i].record(stream)
+        layer.step(qs[(step - 1) % nq], step)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kernel_s = float(np.mean(kern_ms)) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = args.steps / wall
+    algo = algorithmic_bytes(cfg, ctx)
+    achieved = algo["total"] / avg_kernel_s / 1e9
+    admits = int(layer.admit_count.sum().item())
+    log(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms: {value:.1f} layer-steps/s; kernel avg "
+        f"{avg_kernel_s * 1e6:.1f} us (min {min(kern_ms) * 1e3:.1f}), {achieved:.0f} GB/s; "
+        f"last step admitted {admits} blocks")
+
+    result = {
+        "metric": "look-ahead layer-steps/s (batch 128, 16K ctx) + achieved HBM GB/s % of peak",
+        "value": round(value, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: one look-ahead layer step (attention + draft scan + "
+                               f"top-K + capped eviction)",
+                   "batch": cfg.batch, "ctx": int(ctx.max()), "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "k_resident": cfg.k_resident, "cap": cfg.cap},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(algo["total"]),
+                     "kernel": KERNEL, "algorithmic_bytes_per_launch": algo["total"],
+                     "avg_kernel_us": round(avg_kernel_s * 1e6, 2)},
+    }
+
+    if not args.no_pcie:
+        # prefetch leg: the blocks the last step admitted, gather kernel reading
+        # pinned host memory on a side stream, then DMA copies
+        side = torch.cuda.Stream()
+        res = {}
+        nbytes = admits * lib.record_bytes(layer.shape)
+        staging = torch.empty(cfg.batch * cfg.n_kv_heads * (3 * cfg.k_resident + 1),
+                              dtype=torch.int32, pin_memory=True)
+        for name, mode in (("gather", lib.GATHER), ("memcpy", lib.MEMCPY)):
+            ts = []
+            for rep in range(4):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                h0 = time.perf_counter()
+                a.record(side)
+                layer.prefetch(rec_host, mode=mode, host_staging=staging, side_stream=side)
+                b.record(side)
+                torch.cuda.synchronize()
+                ts.append((a.elapsed_time(b) / 1e3, time.perf_counter() - h0))
+            dev_s = float(np.median([t[0] for t in ts[1:]]))
+            host_s = float(np.median([t[1] for t in ts[1:]]))
+            res[name] = {"bytes": nbytes, "device_s": dev_s, "host_s": host_s,
+                         "GBps": round(nbytes / max(host_s, 1e-9) / 1e9, 2)}
+        best = min(r["host_s"] for r in res.values())
+        result["pcie"] = {"admitted_blocks_per_step": admits, "bytes_per_step": nbytes,
+                          "gather": res["gather"], "memcpy": res["memcpy"],
+                          "pcie_inclusive_layer_steps_per_s": round(1.0 / (ms_per_step / 1e3 + best), 2)}
+        log(f"[bench] prefetch {nbytes / 1e6:.1f} MB: gather {res['gather']['GBps']} GB/s, "
+            f"memcpy {res['memcpy']['GBps']} GB/s")
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] oracle baseline on {args.cpu_units} units ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, ctx, rec_host, qs[0].cpu(), args.cpu_units)
+        log(f"[bench] oracle: {result['cpu_baseline']['value']:.3f} layer-steps/s on "
+            f"{result['cpu_baseline']['cores']} threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

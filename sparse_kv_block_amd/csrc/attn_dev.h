@@ -1,0 +1,287 @@
+// Look-ahead attention of one unit (request b, KV head h) by one 256-thread
+// workgroup.  Both query rows (normal and draft) of the G query heads of the KV
+// head are stacked as 2G rows and share every K/V load (pith.science paper
+// page, "What carries the argument": one kernel runs the normal and the draft
+// token over the same resident set).
+//
+// bf16 path: CDNA4 MFMA.  Each wave owns a contiguous range of the unit's
+// slots and streams their 8 KiB block records straight from HBM into
+// registers (no LDS staging: the record layout already matches the operand
+// layout), one block ahead of the math:
+//   logits  D[token][row] = K[token][:] . Q[row][:]   mfma 16x16x32 bf16, d/32 steps
+//   output  O[c][row]    += V^T[c][token] . P[token][row]  mfma 16x16x16 bf16, d/16 tiles
+// The 16x16 logit tile leaves lane (g, n) holding rows n, tokens 4g..4g+3,
+// which is exactly the B operand layout of the 16x16x16 P.V step, so P never
+// leaves registers.  Softmax is online with a lazy rescale: the running max
+// only moves when a block's max exceeds it by more than 8 (in log2 units), so
+// unnormalised weights stay below 2^8.  The four waves' partial (max, sum, O)
+// are merged through LDS at the end.
+//
+// f32 path: plain VALU (one wave per query row); it serves the small fp32
+// workloads whose tolerance is 1e-5.
+#pragma once
+
+#include "common.h"
+
+namespace oasis {
+
+// LDS bytes the bf16 attention merge needs.
+__host__ __device__ constexpr int attn_lds_bytes(int D, int RT) {
+  return (2 * RT * D * 17 + kWaves * 16 * RT * 2 + 16 * RT) * 4;
+}
+__host__ __device__ constexpr int attn_f32_lds_bytes() { return 0; }
+
+template <int D, int RT>
+__device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
+                                               const uint16_t* __restrict__ pool,
+                                               const int32_t* __restrict__ p2l, int b, int h,
+                                               int L, float scale_log2,
+                                               uint16_t* __restrict__ out, float* lds) {
+  constexpr int KS = D / 32;   // logit MFMA steps
+  constexpr int NT = D / 16;   // output tiles
+  constexpr int REC = 2 * kBlock * D;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int G = sh.G;
+  const int unit = b * sh.H + h;
+
+  // Query operand: lane (g, n) holds row 16*rt + n, channels 32*kk + 8g .. +8.
+  bf16x8 qop[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = 16 * rt + n;
+    const bool valid = r < 2 * G;
+    const int row = r < G ? 0 : 1;
+    const int head = h * G + (r < G ? r : r - G);
+    const uint16_t* qr = q + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (valid) {
+        qop[rt][kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qop[rt][kk] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+  }
+
+  // This wave's slots and which of them hold a block with valid tokens.
+  const int s0 = (sh.K * w) / kWaves;
+  const int s1 = (sh.K * (w + 1)) / kWaves;
+  int j_l = -1, nv_l = 0;
+  if (lane < s1 - s0) {
+    j_l = p2l[(size_t)unit * sh.K + s0 + lane];
+    if (j_l >= 0 && j_l < sh.NBmax) {
+      int nv = L - j_l * kBlock;
+      nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
+    }
+  }
+  uint64_t todo = ballot(nv_l > 0);
+
+  float m_run[RT], l_run[RT];
+  f32x4 acc[RT][NT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const uint16_t* unit_pool = pool + (size_t)unit * sh.K * REC;
+  bf16x8 kc[KS];
+  i16x4 vc[NT];
+  auto load = [&](int slot, bf16x8* kr, i16x4* vr) {
+    const uint16_t* rec = unit_pool + (size_t)slot * REC;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      kr[kk] = *reinterpret_cast<const bf16x8*>(rec + n * D + 32 * kk + 8 * g);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      vr[nt] = *reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g);
+  };
+
+  if (todo) load(s0 + __builtin_ctzll(todo), kc, vc);
+  while (todo) {
+    const int sl = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int nv = __builtin_amdgcn_readlane(nv_l, sl);
+    bf16x8 kn[KS];
+    i16x4 vn[NT];
+    if (todo) load(s0 + __builtin_ctzll(todo), kn, vn);
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[kk], qop[rt][kk], z, 0, 0, 0);
+      float zz[4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zz[i] = (4 * g + i < nv) ? z[i] * scale_log2 : -INFINITY;
+        bm = fmaxf(bm, zz[i]);
+      }
+      bm = xrow_max(bm);
+      const bool need = bm > m_run[rt] + 8.0f;
+      if (ballot(need)) {
+        const float f = need ? exp2f(m_run[rt] - bm) : 1.0f;
+        if (need) m_run[rt] = bm;
+        l_run[rt] *= f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rt][nt] *= f;
+      }
+      i16x4 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t hb = f32_to_bf16_bits(exp2f(zz[i] - m_run[rt]));
+        pb[i] = (short)hb;
+        l_run[rt] += bf16_bits_to_f32(hb);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vc[nt], pb, acc[rt][nt], 0, 0, 0);
+    }
+    if (todo) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) kc[kk] = kn[kk];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vc[nt] = vn[nt];
+    }
+  }
+
+  // ---- merge the four waves ----
+  float* obuf = lds;                                   // [2][RT][D][17]
+  float* mbuf = lds + 2 * RT * D * 17;                 // [kWaves][16*RT]
+  float* lbuf = mbuf + kWaves * 16 * RT;               // [kWaves][16*RT]
+  float* lstar = lbuf + kWaves * 16 * RT;              // [16*RT]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float lsum = xrow_sum(l_run[rt]);
+    if (g == 0) {
+      mbuf[w * 16 * RT + 16 * rt + n] = m_run[rt];
+      lbuf[w * 16 * RT + 16 * rt + n] = lsum;
+    }
+  }
+  __syncthreads();
+  float fw[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = 16 * rt + n;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mbuf[v * 16 * RT + r]);
+    float Ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float mv = mbuf[v * 16 * RT + r];
+      const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
+      Ls += lbuf[v * 16 * RT + r] * f;
+      if (v == w) fw[rt] = f;
+    }
+    if (w == 0 && g == 0) lstar[r] = Ls;
+  }
+  // waves 0,1 write their scaled partial outputs; waves 2,3 add theirs
+  for (int phase = 0; phase < 2; ++phase) {
+    if ((w >> 1) == phase) {
+      float* ob = obuf + (w & 1) * RT * D * 17;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 16 * nt + 4 * g + i;
+            float* p = ob + (rt * D + c) * 17 + n;
+            const float v = acc[rt][nt][i] * fw[rt];
+            if (phase == 0) *p = v; else *p += v;
+          }
+    }
+    __syncthreads();
+  }
+  const int rows = 2 * G;
+  for (int e = tid; e < rows * D; e += kThreads) {
+    const int r = e / D, c = e % D;
+    const int rt = r / 16, rr = r % 16;
+    const float o0 = obuf[(rt * D + c) * 17 + rr];
+    const float o1 = obuf[RT * D * 17 + (rt * D + c) * 17 + rr];
+    const float Ls = lstar[r];
+    const float o = Ls > 0.f ? (o0 + o1) / Ls : 0.f;
+    const int row = r < G ? 0 : 1;
+    const int head = h * G + (r < G ? r : r - G);
+    out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(o);
+  }
+}
+
+// fp32 look-ahead attention: one wave per query row, 64 tokens (4 slots) per
+// step, online softmax in fp32.
+template <int D>
+__device__ __forceinline__ void attn_unit_f32(const Shape& sh, const float* __restrict__ q,
+                                              const float* __restrict__ pool,
+                                              const int32_t* __restrict__ p2l, int b, int h,
+                                              int L, float scale, float* __restrict__ out) {
+  constexpr int REC = 2 * kBlock * D;
+  constexpr int CPL = (D + kWave - 1) / kWave;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+  const int G = sh.G;
+  const int unit = b * sh.H + h;
+  const float* unit_pool = pool + (size_t)unit * sh.K * REC;
+  for (int r = w; r < 2 * G; r += kWaves) {
+    const int row = r < G ? 0 : 1;
+    const int head = h * G + (r < G ? r : r - G);
+    const float* qr = q + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
+    float m = -INFINITY, lsum = 0.f;
+    float acc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+    for (int sb = 0; sb < sh.K; sb += 4) {
+      const int s = sb + lane / kBlock;
+      const int u = lane % kBlock;
+      int j = -1;
+      if (s < sh.K) j = p2l[(size_t)unit * sh.K + s];
+      const bool valid = s < sh.K && j >= 0 && j < sh.NBmax && j * kBlock + u < L;
+      float z = -INFINITY;
+      if (valid) {
+        const float* kr = unit_pool + (size_t)s * REC + u * D;
+        float dot = 0.f;
+        for (int c = 0; c < D; ++c) dot = fmaf(qr[c], kr[c], dot);
+        z = dot * scale;
+      }
+      const float cm = wave_max(z);
+      if (cm == -INFINITY) continue;
+      const float nm = fmaxf(m, cm);
+      const float f = (m == -INFINITY) ? 0.f : expf(m - nm);
+      m = nm;
+      lsum *= f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[i] *= f;
+      const float p = valid ? expf(z - m) : 0.f;
+      lsum += wave_sum(p);
+      for (int t = 0; t < kWave; ++t) {
+        const float pt = __shfl(p, t);
+        if (pt == 0.f) continue;
+        const int st = sb + t / kBlock, ut = t % kBlock;
+        const float* vr = unit_pool + (size_t)st * REC + kBlock * D;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = lane + kWave * i;
+          if (c < D) acc[i] = fmaf(pt, vr[c * kBlock + ut], acc[i]);
+        }
+      }
+    }
+    float* orow = out + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + kWave * i;
+      if (c < D) orow[c] = lsum > 0.f ? acc[i] / lsum : 0.f;
+    }
+  }
+}
+
+}  // namespace oasis

@@ -1,0 +1,100 @@
+// Device helpers shared by the gfx950 kernels: element loads, bf16 packing,
+// wave64 reductions and orderable score keys.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oasis {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;      // tokens per KV block
+constexpr int kThreads = 256;   // threads per workgroup (4 waves) in every per-unit kernel
+constexpr int kWaves = kThreads / kWave;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Shape {
+  int B, Hq, H, G, d, NBmax, K;
+};
+
+__device__ __forceinline__ int n_blocks(int L, int NBmax) {
+  if (L <= 0) return 0;
+  int nb = (L + kBlock - 1) / kBlock;
+  return nb < NBmax ? nb : NBmax;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// DPP lane moves inside a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+
+// Max / sum over lanes l, l^16, l^32, l^48 (the four lanes that share l % 16).
+__device__ __forceinline__ float xrow_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float xrow_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key); -0 and +0
+// map to the same key.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+}  // namespace oasis

@@ -1,0 +1,351 @@
+// gfx950 kernels of the look-ahead sparse decode step and their launchers.
+//
+// Every per-unit kernel runs one 256-thread workgroup per (request, KV head):
+// the units are independent (their blocks, summaries, maps and slots are
+// disjoint), so nothing crosses workgroups and the launch needs no inter-block
+// synchronisation.  At batch 128 x 8 KV heads that is 1024 workgroups, four
+// per CU on the 256 CUs, all resident at once.
+#include "attn_dev.h"
+#include "launch.h"
+#include "select_dev.h"
+
+namespace oasis {
+
+// ------------------------------------------------------------------ summaries
+// One wave per block: lane (g, n) takes channels n*D/16 .. +D/16 of tokens
+// g, g+4, g+8, g+12; the four token groups are merged with lane exchanges.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void summarize_kernel(Shape sh, const T* __restrict__ rec,
+                                                             const int32_t* __restrict__ ctx,
+                                                             T* __restrict__ summ) {
+  constexpr int CPL = D / 16;
+  const int unit = blockIdx.y;
+  const int b = unit / sh.H;
+  const int L = ctx[b];
+  const int nb = n_blocks(L, sh.NBmax);
+  const int w = threadIdx.x / kWave;
+  const int j = blockIdx.x * kWaves + w;
+  if (j >= nb) return;
+  const int lane = threadIdx.x % kWave;
+  const int g = lane >> 4, n = lane & 15;
+  const int c0 = n * CPL;
+  int nv = L - j * kBlock;
+  nv = nv > kBlock ? kBlock : nv;
+  const T* blk = rec + ((size_t)unit * sh.NBmax + j) * (2 * kBlock * D);
+  float mn[CPL], mx[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) { mn[c] = INFINITY; mx[c] = -INFINITY; }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = g + 4 * i;
+    if (u < nv) {
+      float v[CPL];
+      Elem<T>::template load<CPL>(blk + u * D + c0, v);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) { mn[c] = fminf(mn[c], v[c]); mx[c] = fmaxf(mx[c], v[c]); }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    mn[c] = fminf(mn[c], __shfl_xor(mn[c], 16));
+    mn[c] = fminf(mn[c], __shfl_xor(mn[c], 32));
+    mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 16));
+    mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 32));
+  }
+  if (g == 0) {
+    T* out = summ + ((size_t)unit * sh.NBmax + j) * 2 * D + c0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      if constexpr (sizeof(T) == 2) {
+        out[c] = f32_to_bf16_bits(mn[c]);
+        out[D + c] = f32_to_bf16_bits(mx[c]);
+      } else {
+        out[c] = mn[c];
+        out[D + c] = mx[c];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+template <int D, int RT>
+__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(Shape sh, const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ pool,
+                                                             const int32_t* __restrict__ p2l,
+                                                             const int32_t* __restrict__ ctx,
+                                                             float scale_log2,
+                                                             uint16_t* __restrict__ out) {
+  extern __shared__ __align__(16) char smem[];
+  const int unit = blockIdx.x;
+  const int b = unit / sh.H, h = unit % sh.H;
+  attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, ctx[b], scale_log2, out,
+                        reinterpret_cast<float*>(smem));
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(Shape sh, const float* __restrict__ q,
+                                                            const float* __restrict__ pool,
+                                                            const int32_t* __restrict__ p2l,
+                                                            const int32_t* __restrict__ ctx,
+                                                            float scale, float* __restrict__ out) {
+  const int unit = blockIdx.x;
+  const int b = unit / sh.H, h = unit % sh.H;
+  attn_unit_f32<D>(sh, q, pool, p2l, b, h, ctx[b], scale, out);
+}
+
+// ------------------------------------------------------------------ scan + top-K
+struct SelectPtrs {
+  uint32_t* keys;
+  int* cand_idx;
+  uint32_t* cand_key;
+  int* sel_idx;
+  uint32_t* sel_key;
+  EvictScratch ev;
+};
+
+__device__ __forceinline__ SelectPtrs select_ptrs(char* smem, int NBmax, int K) {
+  SelectLds lay(NBmax, K);
+  SelectPtrs p;
+  p.keys = reinterpret_cast<uint32_t*>(smem + lay.keys);
+  p.cand_idx = reinterpret_cast<int*>(smem + lay.cand_idx);
+  p.cand_key = reinterpret_cast<uint32_t*>(smem + lay.cand_key);
+  p.sel_idx = reinterpret_cast<int*>(smem + lay.sel_idx);
+  p.sel_key = reinterpret_cast<uint32_t*>(smem + lay.sel_key);
+  p.ev.p2l_s = reinterpret_cast<int*>(smem + lay.p2l_s);
+  p.ev.ls_s = reinterpret_cast<int*>(smem + lay.ls_s);
+  p.ev.miss = reinterpret_cast<int*>(smem + lay.miss);
+  p.ev.victim = reinterpret_cast<int*>(smem + lay.victim);
+  p.ev.vkey = reinterpret_cast<uint64_t*>(smem + lay.vkey);
+  p.ev.red = reinterpret_cast<int*>(smem + lay.red);
+  return p;
+}
+
+// Scan + select for one unit; leaves the sorted list in p.sel_idx (entries
+// past kk set to -1) and writes the top-K outputs.
+template <typename T, int D>
+__device__ __forceinline__ void select_unit(const Shape& sh, const T* q, int q_row, const T* summ,
+                                            int unit, int L, int32_t* topk_idx, float* topk_score,
+                                            const SelectPtrs& p) {
+  const int b = unit / sh.H, h = unit % sh.H;
+  const int nb = n_blocks(L, sh.NBmax);
+  scan_unit<T, D>(sh, q, q_row, summ + (size_t)unit * sh.NBmax * 2 * D, b, h, nb, p.keys);
+  __syncthreads();
+  const int kk = topk_unit(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  for (int t = threadIdx.x; t < sh.K; t += kThreads) {
+    if (t >= kk) p.sel_idx[t] = -1;
+    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
+    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
+  }
+  __syncthreads();
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T* __restrict__ q,
+                                                              int q_row, const T* __restrict__ summ,
+                                                              const int32_t* __restrict__ ctx,
+                                                              int32_t* __restrict__ topk_idx,
+                                                              float* __restrict__ topk_score) {
+  extern __shared__ __align__(16) char smem[];
+  const int unit = blockIdx.x;
+  const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
+  select_unit<T, D>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
+}
+
+// ------------------------------------------------------------------ eviction
+__global__ __launch_bounds__(kThreads) void evict_kernel(Shape sh, const int32_t* __restrict__ topk_idx,
+                                                         int step, int max_admit, int32_t* l2p,
+                                                         int32_t* p2l, int32_t* last_sel,
+                                                         int32_t* admit, int32_t* admit_count) {
+  extern __shared__ __align__(16) char smem[];
+  const int unit = blockIdx.x;
+  const SelectPtrs p = select_ptrs(smem, 0, sh.K);
+  evict_unit(topk_idx + (size_t)unit * sh.K, sh.K, sh.NBmax, step, max_admit,
+             l2p + (size_t)unit * sh.NBmax, p2l + (size_t)unit * sh.K,
+             last_sel + (size_t)unit * sh.K, admit + (size_t)unit * sh.K * 3, admit_count + unit,
+             p.ev);
+}
+
+// ------------------------------------------------------------------ prefetch
+// One workgroup per (unit, admission): copies one whole record with 16-byte
+// loads; the source may be host-mapped pinned memory (read over the host link).
+__global__ __launch_bounds__(kThreads) void prefetch_gather_kernel(int K, int NBmax, int rec_bytes,
+                                                                   const uint8_t* __restrict__ rec,
+                                                                   uint8_t* __restrict__ pool,
+                                                                   const int32_t* __restrict__ admit,
+                                                                   const int32_t* __restrict__ admit_count) {
+  const int unit = blockIdx.x;
+  const int k = blockIdx.y;
+  if (k >= admit_count[unit]) return;
+  const int32_t* a = admit + ((size_t)unit * K + k) * 3;
+  const int j = a[0], s = a[1];
+  if (j < 0 || j >= NBmax || s < 0 || s >= K) return;
+  const uint8_t* src = rec + ((size_t)unit * NBmax + j) * rec_bytes;
+  uint8_t* dst = pool + ((size_t)unit * K + s) * rec_bytes;
+  for (int off = threadIdx.x * 16; off < rec_bytes; off += kThreads * 16)
+    *reinterpret_cast<u32x4*>(dst + off) = *reinterpret_cast<const u32x4*>(src + off);
+}
+
+// ------------------------------------------------------------------ fused layer step
+template <int D, int RT>
+__global__ __launch_bounds__(kThreads) void layer_step_bf16_kernel(
+    Shape sh, const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
+    const uint16_t* __restrict__ summ, const int32_t* __restrict__ ctx, float scale_log2, int step,
+    int max_admit, uint16_t* __restrict__ out, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+    int32_t* admit_count) {
+  extern __shared__ __align__(16) char smem[];
+  const int unit = blockIdx.x;
+  const int b = unit / sh.H, h = unit % sh.H;
+  const int L = ctx[b];
+  attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale_log2, out, reinterpret_cast<float*>(smem));
+  __syncthreads();
+  const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
+  select_unit<uint16_t, D>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+  evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
+             p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
+             admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void layer_step_f32_kernel(
+    Shape sh, const float* __restrict__ q, const float* __restrict__ pool,
+    const float* __restrict__ summ, const int32_t* __restrict__ ctx, float scale, int step,
+    int max_admit, float* __restrict__ out, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+    int32_t* admit_count) {
+  extern __shared__ __align__(16) char smem[];
+  const int unit = blockIdx.x;
+  const int b = unit / sh.H, h = unit % sh.H;
+  const int L = ctx[b];
+  attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
+  __syncthreads();
+  const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
+  select_unit<float, D>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+  evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
+             p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
+             admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+}
+
+// ------------------------------------------------------------------ launchers
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+
+float scale_or_default(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+int rt_of(int G) { return 2 * G <= 16 ? 1 : 2; }
+}  // namespace
+
+hipError_t launch_summarize(const Shape& sh, int dtype, const void* records, const int32_t* ctx,
+                            void* summ, hipStream_t st) {
+  dim3 grid((sh.NBmax + kWaves - 1) / kWaves, sh.B * sh.H);
+  if (dtype == 1) {
+    if (sh.d == 128)
+      hipLaunchKernelGGL((summarize_kernel<uint16_t, 128>), grid, dim3(kThreads), 0, st, sh,
+                         (const uint16_t*)records, ctx, (uint16_t*)summ);
+    else
+      hipLaunchKernelGGL((summarize_kernel<uint16_t, 64>), grid, dim3(kThreads), 0, st, sh,
+                         (const uint16_t*)records, ctx, (uint16_t*)summ);
+  } else {
+    if (sh.d == 128)
+      hipLaunchKernelGGL((summarize_kernel<float, 128>), grid, dim3(kThreads), 0, st, sh,
+                         (const float*)records, ctx, (float*)summ);
+    else
+      hipLaunchKernelGGL((summarize_kernel<float, 64>), grid, dim3(kThreads), 0, st, sh,
+                         (const float*)records, ctx, (float*)summ);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const Shape& sh, int dtype, const void* q, const void* pool,
+                       const int32_t* p2l, const int32_t* ctx, float scale, void* out,
+                       hipStream_t st) {
+  const float sc = scale_or_default(scale, sh.d);
+  dim3 grid(sh.B * sh.H);
+  if (dtype == 1) {
+    const int rt = rt_of(sh.G);
+    const size_t lds = attn_lds_bytes(sh.d, rt);
+    const float sl = sc * kLog2e;
+#define OASIS_ATTN(D_, RT_)                                                                   \
+  hipLaunchKernelGGL((attn_bf16_kernel<D_, RT_>), grid, dim3(kThreads), lds, st, sh,          \
+                     (const uint16_t*)q, (const uint16_t*)pool, p2l, ctx, sl, (uint16_t*)out)
+    if (sh.d == 128) { if (rt == 1) OASIS_ATTN(128, 1); else OASIS_ATTN(128, 2); }
+    else             { if (rt == 1) OASIS_ATTN(64, 1);  else OASIS_ATTN(64, 2); }
+#undef OASIS_ATTN
+  } else {
+    if (sh.d == 128)
+      hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(kThreads), 0, st, sh,
+                         (const float*)q, (const float*)pool, p2l, ctx, sc, (float*)out);
+    else
+      hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(kThreads), 0, st, sh,
+                         (const float*)q, (const float*)pool, p2l, ctx, sc, (float*)out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_topk(const Shape& sh, int dtype, const void* q, int q_row, const void* summ,
+                             const int32_t* ctx, int32_t* topk_idx, float* topk_score,
+                             hipStream_t st) {
+  dim3 grid(sh.B * sh.H);
+  const size_t lds = SelectLds(sh.NBmax, sh.K).total;
+#define OASIS_SCORE(T_, D_)                                                                   \
+  hipLaunchKernelGGL((score_topk_kernel<T_, D_>), grid, dim3(kThreads), lds, st, sh,          \
+                     (const T_*)q, q_row, (const T_*)summ, ctx, topk_idx, topk_score)
+  if (dtype == 1) { if (sh.d == 128) OASIS_SCORE(uint16_t, 128); else OASIS_SCORE(uint16_t, 64); }
+  else            { if (sh.d == 128) OASIS_SCORE(float, 128);    else OASIS_SCORE(float, 64); }
+#undef OASIS_SCORE
+  return hipGetLastError();
+}
+
+hipError_t launch_evict(const Shape& sh, const int32_t* topk_idx, int step, int max_admit,
+                        int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                        int32_t* admit_count, hipStream_t st) {
+  const size_t lds = SelectLds(0, sh.K).total;
+  hipLaunchKernelGGL(evict_kernel, dim3(sh.B * sh.H), dim3(kThreads), lds, st, sh, topk_idx, step,
+                     max_admit, l2p, p2l, last_sel, admit, admit_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefetch_gather(const Shape& sh, size_t rec_bytes, const void* records, void* pool,
+                                  const int32_t* admit, const int32_t* admit_count, int max_admit,
+                                  hipStream_t st) {
+  if (max_admit <= 0) return hipSuccess;
+  dim3 grid(sh.B * sh.H, max_admit);
+  hipLaunchKernelGGL(prefetch_gather_kernel, grid, dim3(kThreads), 0, st, sh.K, sh.NBmax,
+                     (int)rec_bytes, (const uint8_t*)records, (uint8_t*)pool, admit, admit_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const void* pool,
+                             const void* summ, const int32_t* ctx, float scale, int step,
+                             int max_admit, void* out, int32_t* topk_idx, float* topk_score,
+                             int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                             int32_t* admit_count, hipStream_t st) {
+  const float sc = scale_or_default(scale, sh.d);
+  dim3 grid(sh.B * sh.H);
+  const size_t sel = SelectLds(sh.NBmax, sh.K).total;
+  if (dtype == 1) {
+    const int rt = rt_of(sh.G);
+    const size_t att = attn_lds_bytes(sh.d, rt);
+    const size_t lds = att > sel ? att : sel;
+    const float sl = sc * kLog2e;
+#define OASIS_STEP(D_, RT_)                                                                   \
+  hipLaunchKernelGGL((layer_step_bf16_kernel<D_, RT_>), grid, dim3(kThreads), lds, st, sh,    \
+                     (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ, ctx, sl, \
+                     step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l, last_sel, \
+                     admit, admit_count)
+    if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1); else OASIS_STEP(128, 2); }
+    else             { if (rt == 1) OASIS_STEP(64, 1);  else OASIS_STEP(64, 2); }
+#undef OASIS_STEP
+  } else {
+#define OASIS_STEP32(D_)                                                                      \
+  hipLaunchKernelGGL((layer_step_f32_kernel<D_>), grid, dim3(kThreads), sel, st, sh,          \
+                     (const float*)q, (const float*)pool, (const float*)summ, ctx, sc, step,  \
+                     max_admit, (float*)out, topk_idx, topk_score, l2p, p2l, last_sel, admit, \
+                     admit_count)
+    if (sh.d == 128) OASIS_STEP32(128); else OASIS_STEP32(64);
+#undef OASIS_STEP32
+  }
+  return hipGetLastError();
+}
+
+}  // namespace oasis

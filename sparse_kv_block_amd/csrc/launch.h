@@ -1,0 +1,32 @@
+// Internal launchers: the kernels' translation unit exports these to the
+// C-ABI layer.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace oasis {
+
+struct Shape;
+
+hipError_t launch_summarize(const Shape& sh, int dtype, const void* records,
+                            const int32_t* ctx_len, void* summ, hipStream_t st);
+hipError_t launch_attn(const Shape& sh, int dtype, const void* q, const void* pool,
+                       const int32_t* p2l, const int32_t* ctx_len, float scale, void* out,
+                       hipStream_t st);
+hipError_t launch_score_topk(const Shape& sh, int dtype, const void* q, int q_row,
+                             const void* summ, const int32_t* ctx_len, int32_t* topk_idx,
+                             float* topk_score, hipStream_t st);
+hipError_t launch_evict(const Shape& sh, const int32_t* topk_idx, int step, int max_admit,
+                        int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                        int32_t* admit_count, hipStream_t st);
+hipError_t launch_prefetch_gather(const Shape& sh, size_t rec_bytes, const void* records,
+                                  void* pool, const int32_t* admit, const int32_t* admit_count,
+                                  int max_admit, hipStream_t st);
+hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const void* pool,
+                             const void* summ, const int32_t* ctx_len, float scale, int step,
+                             int max_admit, void* out, int32_t* topk_idx, float* topk_score,
+                             int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                             int32_t* admit_count, hipStream_t st);
+
+}  // namespace oasis

@@ -1,0 +1,333 @@
+// Summary scan, top-K selection and capped eviction of one unit (request b,
+// KV head h) by one 256-thread workgroup.
+//
+// Scan (pith.science paper page, "What carries the argument": the draft query
+// scans per-block min/max key summaries and ranks every logical block per KV
+// head).  The group score of block j is
+//     sum_i sum_c max(q_ic * min_jc, q_ic * max_jc),
+// which for min <= max equals sum_c [(min+max)/2 * Q_c + (max-min)/2 * A_c]
+// with Q_c = sum_i q_ic and A_c = sum_i |q_ic|: two FMAs per channel per block
+// instead of 2G.  Sixteen lanes share one 512-byte bf16 summary record (8
+// channels each, one 16-byte load of the min row and one of the max row) and
+// reduce with DPP inside their 16-lane row; a wave covers 4 blocks per load.
+// The scores of the unit's whole context stay in LDS as order-preserving
+// 32-bit keys.
+//
+// Top-K: MSB-first radix bisection on the keys, counting with wave ballots
+// (popcount) and one LDS exchange per bit, finds the K-th largest key T; keys
+// above T and the lowest-index keys equal to T are compacted and ranked by
+// (score desc, block asc).
+//
+// Capped eviction (same page: admissions per step are capped and each
+// admitted block is paired with a least-recently-selected resident block):
+// hits are stamped, misses compacted in top-K order with ballots, victims
+// (empty slots first, then stale slots by (stamp, block)) ranked by a 64-bit
+// key, and the maps updated.
+#pragma once
+
+#include "common.h"
+
+namespace oasis {
+
+// ---------------------------------------------------------------- summary scan
+template <typename T>
+struct Elem;
+template <>
+struct Elem<uint16_t> {
+  // load n consecutive bf16 values (n = 4 or 8) as fp32
+  template <int N>
+  __device__ static __forceinline__ void load(const uint16_t* p, float* v) {
+    if constexpr (N == 8) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+    }
+  }
+  __device__ static __forceinline__ float one(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+};
+template <>
+struct Elem<float> {
+  template <int N>
+  __device__ static __forceinline__ void load(const float* p, float* v) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(p + i);
+      v[i] = w[0]; v[i + 1] = w[1]; v[i + 2] = w[2]; v[i + 3] = w[3];
+    }
+  }
+  __device__ static __forceinline__ float one(const float* p) { return *p; }
+};
+
+// Writes keys[j] for j < nb.  summ_unit points at the unit's [NBmax][2][D].
+template <typename T, int D>
+__device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__ q, int q_row,
+                                          const T* __restrict__ summ_unit, int b, int h, int nb,
+                                          uint32_t* keys) {
+  constexpr int CPL = D / 16;   // channels per lane
+  constexpr int U = 4;          // blocks in flight per lane group
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+  const int quad = lane >> 4;
+  const int n = lane & 15;
+  const int c0 = n * CPL;
+
+  float Qh[CPL], Ah[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) { Qh[i] = 0.f; Ah[i] = 0.f; }
+  for (int i = 0; i < sh.G; ++i) {
+    float v[CPL];
+    Elem<T>::template load<CPL>(q + ((size_t)(b * 2 + q_row) * sh.Hq + h * sh.G + i) * D + c0, v);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) { Qh[c] += v[c]; Ah[c] += fabsf(v[c]); }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) { Qh[c] *= 0.5f; Ah[c] *= 0.5f; }
+
+  for (int jb = w * 4; jb < nb; jb += kThreads / 16 * U) {
+    float part[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + quad + (kThreads / 16) * u;
+      float lo[CPL], hi[CPL];
+      if (j < nb) {
+        const T* rec = summ_unit + (size_t)j * 2 * D + c0;
+        Elem<T>::template load<CPL>(rec, lo);
+        Elem<T>::template load<CPL>(rec + D, hi);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) { lo[c] = 0.f; hi[c] = 0.f; }
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        s = fmaf(lo[c] + hi[c], Qh[c], s);
+        s = fmaf(hi[c] - lo[c], Ah[c], s);
+      }
+      part[u] = s;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float s = row16_sum(part[u]);
+      const int j = jb + quad + (kThreads / 16) * u;
+      if (n == 0 && j < nb) keys[j] = score_key(s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-K
+// Scratch (LDS ints): red[2][kWaves] + 4 extra.
+__device__ __forceinline__ int block_count(bool pred, int* red, int parity) {
+  const int w = threadIdx.x / kWave;
+  const uint64_t m = ballot(pred);
+  if (lane_id() == 0) red[parity * kWaves + w] = __popcll(m);
+  __syncthreads();
+  int c = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) c += red[parity * kWaves + v];
+  return c;
+}
+
+// Selects the min(K, nb) best keys; writes sel_idx[0..kk) / sel_key[0..kk) in
+// (key desc, index asc) order and returns kk.  cand_* are K-entry scratch.
+__device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, int* sel_idx,
+                                         uint32_t* sel_key, int* cand_idx, uint32_t* cand_key,
+                                         int* red) {
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int kk = K < nb ? K : nb;
+  if (kk <= 0) return 0;
+  // 1. K-th largest key by MSB-first bisection: T = max{v : #{key >= v} >= kk}.
+  uint32_t T = 0;
+  int parity = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int cnt = 0;
+    for (int base = 0; base < nb; base += kThreads) {
+      const int j = base + tid;
+      const uint64_t m = ballot(j < nb && keys[j] >= cand);
+      cnt += __popcll(m);
+    }
+    if (lane_id() == 0) red[parity * kWaves + w] = cnt;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) tot += red[parity * kWaves + v];
+    if (tot >= kk) T = cand;
+    parity ^= 1;
+  }
+  // 2. compact: keys > T anywhere, then the lowest-index keys == T.
+  int* cnt_gt = red + 2 * kWaves;    // shared counter
+  if (tid == 0) *cnt_gt = 0;
+  __syncthreads();
+  for (int base = 0; base < nb; base += kThreads) {
+    const int j = base + tid;
+    if (j < nb && keys[j] > T) {
+      const int p = atomicAdd(cnt_gt, 1);
+      cand_idx[p] = j;
+      cand_key[p] = keys[j];
+    }
+  }
+  __syncthreads();
+  const int ngt = *cnt_gt;
+  const int need = kk - ngt;
+  int taken = 0;
+  for (int base = 0; base < nb && taken < need; base += kThreads) {
+    const int j = base + tid;
+    const bool eq = j < nb && keys[j] == T;
+    const uint64_t m = ballot(eq);
+    if (lane_id() == 0) red[parity * kWaves + w] = __popcll(m);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const int c = red[parity * kWaves + v];
+      off += v < w ? c : 0;
+      tot += c;
+    }
+    const int r = taken + off + lanes_below(m);
+    if (eq && r < need) {
+      cand_idx[ngt + r] = j;
+      cand_key[ngt + r] = T;
+    }
+    taken += tot;
+    parity ^= 1;
+  }
+  __syncthreads();
+  // 3. rank the kk candidates by (key desc, index asc).
+  if (tid < kk) {
+    const uint32_t k = cand_key[tid];
+    const int j = cand_idx[tid];
+    int rank = 0;
+    for (int p = 0; p < kk; ++p) {
+      const uint32_t kp = cand_key[p];
+      const int jp = cand_idx[p];
+      rank += (kp > k) || (kp == k && jp < j);
+    }
+    sel_idx[rank] = j;
+    sel_key[rank] = k;
+  }
+  __syncthreads();
+  return kk;
+}
+
+// ---------------------------------------------------------------- capped eviction
+struct EvictScratch {
+  int* p2l_s;      // [K]
+  int* ls_s;       // [K]
+  int* miss;       // [K]
+  int* victim;     // [K]
+  uint64_t* vkey;  // [K]
+  int* red;        // [2*kWaves + 4]
+};
+
+// T: the unit's top-K list in LDS or global memory ([K], -1 = unused entry).
+// Pointers l2p/p2l/ls/admit are the unit's slices.
+__device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int step,
+                                           int max_admit, int32_t* __restrict__ l2p,
+                                           int32_t* __restrict__ p2l, int32_t* __restrict__ ls,
+                                           int32_t* __restrict__ admit,
+                                           int32_t* __restrict__ admit_count,
+                                           const EvictScratch& x) {
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  if (tid < K) {
+    x.p2l_s[tid] = p2l[tid];
+    x.ls_s[tid] = ls[tid];
+  }
+  __syncthreads();
+  // 1. stamp resident members of T; flag the missing ones
+  const int j = tid < K ? T[tid] : -1;
+  const bool valid = j >= 0 && j < NBmax;
+  const int s = valid ? l2p[j] : -1;
+  const bool hit = valid && s >= 0 && s < K;
+  const bool miss = valid && !hit;
+  if (hit) x.ls_s[s] = step;
+  const uint64_t mm = ballot(miss);
+  if (lane_id() == 0) x.red[w] = __popcll(mm);
+  __syncthreads();
+  int off = 0, nM = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    off += v < w ? x.red[v] : 0;
+    nM += x.red[v];
+  }
+  if (miss) x.miss[off + lanes_below(mm)] = j;
+  // 2. victim keys: empty slots by slot, then stale slots by (stamp, block)
+  uint64_t key = ~0ull;
+  if (tid < K) {
+    const int e = x.p2l_s[tid];
+    const int st = x.ls_s[tid];
+    if (e < 0)
+      key = (uint64_t)tid;
+    else if (st < step)
+      key = (1ull << 63) | ((uint64_t)((uint32_t)st ^ 0x80000000u) << 31) | (uint64_t)(uint32_t)e;
+    x.vkey[tid] = key;
+  }
+  const bool elig = key != ~0ull;
+  const uint64_t me = ballot(elig);
+  if (lane_id() == 0) x.red[kWaves + w] = __popcll(me);
+  __syncthreads();
+  int nV = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) nV += x.red[kWaves + v];
+  int a = max_admit < nM ? max_admit : nM;
+  a = a < nV ? a : nV;
+  a = a < 0 ? 0 : a;
+  if (elig) {
+    int rank = 0;
+    for (int p = 0; p < K; ++p) rank += x.vkey[p] < key;
+    if (rank < a) x.victim[rank] = tid;
+  }
+  __syncthreads();
+  // 3. apply
+  if (tid < a) {
+    const int sv = x.victim[tid];
+    const int old = x.p2l_s[sv];
+    const int aj = x.miss[tid];
+    if (old >= 0 && old < NBmax) l2p[old] = -1;
+    l2p[aj] = sv;
+    x.p2l_s[sv] = aj;
+    x.ls_s[sv] = step;
+    admit[3 * tid + 0] = aj;
+    admit[3 * tid + 1] = sv;
+    admit[3 * tid + 2] = old;
+  } else if (tid < K) {
+    admit[3 * tid + 0] = -1;
+    admit[3 * tid + 1] = -1;
+    admit[3 * tid + 2] = -1;
+  }
+  __syncthreads();
+  if (tid < K) {
+    p2l[tid] = x.p2l_s[tid];
+    ls[tid] = x.ls_s[tid];
+  }
+  if (tid == 0) *admit_count = a;
+}
+
+// LDS layout of the select phase (scan keys + top-K + eviction), in bytes.
+struct SelectLds {
+  int keys, cand_idx, cand_key, sel_idx, sel_key, p2l_s, ls_s, miss, victim, vkey, red, total;
+  __host__ __device__ SelectLds(int NBmax, int K) {
+    int o = 0;
+    auto take = [&](int bytes) { int r = o; o += (bytes + 15) & ~15; return r; };
+    keys = take(NBmax * 4);
+    cand_idx = take(K * 4);
+    cand_key = take(K * 4);
+    sel_idx = take(K * 4);
+    sel_key = take(K * 4);
+    p2l_s = take(K * 4);
+    ls_s = take(K * 4);
+    miss = take(K * 4);
+    victim = take(K * 4);
+    vkey = take(K * 8);
+    red = take((2 * kWaves + 4) * 4);
+    total = o;
+  }
+};
+
+}  // namespace oasis

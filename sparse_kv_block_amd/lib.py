@@ -1,0 +1,218 @@
+"""Thin ctypes binding over liboasis.so (include/oasis.h).
+
+Argument marshalling only: it checks tensor devices, dtypes, contiguity and
+sizes against the shape (so that no kernel is launched over a buffer smaller
+than its grid assumes), then passes raw pointers and the current HIP stream.
+Every step runs in the HIP library; there is no fallback.  Importing this
+module raises if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .configs import Config
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liboasis.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+F32, BF16 = 0, 1
+GATHER, MEMCPY = 0, 1
+
+# every symbol include/oasis.h declares
+SYMBOLS = ("oasis_abi_version", "oasis_last_error", "oasis_cap_to_max_admit",
+           "oasis_record_bytes", "oasis_summary_bytes", "oasis_host_to_device_ptr",
+           "oasis_summarize", "oasis_lookahead_attn", "oasis_score_topk",
+           "oasis_capped_evict", "oasis_prefetch", "oasis_layer_step")
+
+
+class OasisError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[oasis status {status}] {msg}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("k_resident", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    @staticmethod
+    def of(cfg: Config, max_blocks: int, batch: Optional[int] = None) -> "Shape":
+        return Shape(cfg.batch if batch is None else batch, cfg.n_q_heads, cfg.n_kv_heads,
+                     cfg.head_dim, cfg.block_size, max_blocks, cfg.k_resident,
+                     F32 if cfg.dtype == "f32" else BF16)
+
+    def units(self) -> int:
+        return self.batch * self.n_kv_heads
+
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == F32 else torch.bfloat16
+
+    def record_elems(self) -> int:
+        return 2 * self.block_size * self.head_dim
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m sparse_kv_block_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    SP = ctypes.POINTER(Shape)
+    sig = {
+        "oasis_abi_version": ([], I32),
+        "oasis_last_error": ([], ctypes.c_char_p),
+        "oasis_cap_to_max_admit": ([ctypes.c_double, I32], I32),
+        "oasis_record_bytes": ([SP], ctypes.c_size_t),
+        "oasis_summary_bytes": ([SP], ctypes.c_size_t),
+        "oasis_host_to_device_ptr": ([P, ctypes.POINTER(P)], I32),
+        "oasis_summarize": ([SP, P, P, P, P], I32),
+        "oasis_lookahead_attn": ([SP, P, P, P, P, F, P, P], I32),
+        "oasis_score_topk": ([SP, P, I32, P, P, P, P, P], I32),
+        "oasis_capped_evict": ([SP, P, I32, I32, P, P, P, P, P, P], I32),
+        "oasis_prefetch": ([SP, P, P, P, P, I32, I32, P, P, P, P], I32),
+        "oasis_layer_step": ([SP, P, P, P, P, F, I32, I32, P, P, P, P, P, P, P, P, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+_lib = _load()
+
+
+def raw():
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.oasis_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise OasisError(status, last_error())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype, numel: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the shape needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _any(t: torch.Tensor, name: str, dtype, numel: int):
+    """A device tensor, or a pinned host tensor passed through its device mapping."""
+    if isinstance(t, torch.Tensor) and t.device.type == "cpu":
+        if t.dtype != dtype or not t.is_contiguous() or t.numel() != numel:
+            raise ValueError(f"{name}: wrong dtype, layout or size")
+        if not t.is_pinned():
+            raise ValueError(f"{name}: host memory must be pinned")
+        return ctypes.c_void_p(host_device_ptr(t))
+    return _dev(t, name, dtype, numel)
+
+
+def host_device_ptr(t: torch.Tensor) -> int:
+    out = ctypes.c_void_p()
+    _check(_lib.oasis_host_to_device_ptr(ctypes.c_void_p(t.data_ptr()), ctypes.byref(out)))
+    return out.value
+
+
+def cap_to_max_admit(cap: float, k_resident: int) -> int:
+    return int(_lib.oasis_cap_to_max_admit(float(cap), int(k_resident)))
+
+
+def record_bytes(shape: Shape) -> int:
+    return int(_lib.oasis_record_bytes(ctypes.byref(shape)))
+
+
+I32 = torch.int32
+
+
+def summarize(shape: Shape, records, ctx_len, summ, stream=None):
+    dt, U, NB, d = shape.torch_dtype(), shape.units(), shape.max_blocks, shape.head_dim
+    _check(_lib.oasis_summarize(
+        ctypes.byref(shape), _any(records, "records", dt, U * NB * shape.record_elems()),
+        _dev(ctx_len, "ctx_len", I32, shape.batch), _dev(summ, "summ", dt, U * NB * 2 * d),
+        _stream(stream)))
+
+
+def lookahead_attn(shape: Shape, q, pool, p2l, ctx_len, out, scale: float = 0.0, stream=None):
+    dt, U, K, d = shape.torch_dtype(), shape.units(), shape.k_resident, shape.head_dim
+    qn = shape.batch * 2 * shape.n_q_heads * d
+    _check(_lib.oasis_lookahead_attn(
+        ctypes.byref(shape), _dev(q, "q", dt, qn), _dev(pool, "pool", dt, U * K * shape.record_elems()),
+        _dev(p2l, "p2l", I32, U * K), _dev(ctx_len, "ctx_len", I32, shape.batch), float(scale),
+        _dev(out, "out", dt, qn), _stream(stream)))
+
+
+def score_topk(shape: Shape, q, summ, ctx_len, topk_idx, topk_score, q_row: int = 1, stream=None):
+    dt, U, K, d = shape.torch_dtype(), shape.units(), shape.k_resident, shape.head_dim
+    _check(_lib.oasis_score_topk(
+        ctypes.byref(shape), _dev(q, "q", dt, shape.batch * 2 * shape.n_q_heads * d), int(q_row),
+        _dev(summ, "summ", dt, U * shape.max_blocks * 2 * d),
+        _dev(ctx_len, "ctx_len", I32, shape.batch), _dev(topk_idx, "topk_idx", I32, U * K),
+        _dev(topk_score, "topk_score", torch.float32, U * K), _stream(stream)))
+
+
+def capped_evict(shape: Shape, topk_idx, step: int, max_admit: int, l2p, p2l, last_sel, admit,
+                 admit_count, stream=None):
+    U, K = shape.units(), shape.k_resident
+    _check(_lib.oasis_capped_evict(
+        ctypes.byref(shape), _dev(topk_idx, "topk_idx", I32, U * K), int(step), int(max_admit),
+        _dev(l2p, "l2p", I32, U * shape.max_blocks), _dev(p2l, "p2l", I32, U * K),
+        _dev(last_sel, "last_sel", I32, U * K), _dev(admit, "admit", I32, U * K * 3),
+        _dev(admit_count, "admit_count", I32, U), _stream(stream)))
+
+
+def prefetch(shape: Shape, records, pool, admit, admit_count, max_admit: int, mode: int = GATHER,
+             host_staging=None, side_stream=None, wait_before=None, done=None):
+    dt, U, K = shape.torch_dtype(), shape.units(), shape.k_resident
+    stg = None
+    if mode == MEMCPY:
+        n = U * (3 * K + 1)
+        if (host_staging is None or host_staging.device.type != "cpu" or not host_staging.is_pinned()
+                or host_staging.dtype != I32 or host_staging.numel() < n):
+            raise ValueError(f"MEMCPY mode needs a pinned int32 host_staging of >= {n} elements")
+        stg = ctypes.c_void_p(host_staging.data_ptr())
+    ev = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+    _check(_lib.oasis_prefetch(
+        ctypes.byref(shape), _any(records, "records", dt, U * shape.max_blocks * shape.record_elems()),
+        _dev(pool, "pool", dt, U * K * shape.record_elems()), _dev(admit, "admit", I32, U * K * 3),
+        _dev(admit_count, "admit_count", I32, U), int(max_admit), int(mode), stg,
+        _stream(side_stream), ev(wait_before), ev(done)))
+
+
+def layer_step(shape: Shape, q, pool, summ, ctx_len, step: int, max_admit: int, out, topk_idx,
+               topk_score, l2p, p2l, last_sel, admit, admit_count, scale: float = 0.0, stream=None):
+    dt, U, K, d = shape.torch_dtype(), shape.units(), shape.k_resident, shape.head_dim
+    qn = shape.batch * 2 * shape.n_q_heads * d
+    _check(_lib.oasis_layer_step(
+        ctypes.byref(shape), _dev(q, "q", dt, qn), _dev(pool, "pool", dt, U * K * shape.record_elems()),
+        _dev(summ, "summ", dt, U * shape.max_blocks * 2 * d), _dev(ctx_len, "ctx_len", I32, shape.batch),
+        float(scale), int(step), int(max_admit), _dev(out, "out", dt, qn),
+        _dev(topk_idx, "topk_idx", I32, U * K), _dev(topk_score, "topk_score", torch.float32, U * K),
+        _dev(l2p, "l2p", I32, U * shape.max_blocks), _dev(p2l, "p2l", I32, U * K),
+        _dev(last_sel, "last_sel", I32, U * K), _dev(admit, "admit", I32, U * K * 3),
+        _dev(admit_count, "admit_count", I32, U), _stream(stream)))

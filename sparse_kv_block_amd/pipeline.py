@@ -1,0 +1,87 @@
+"""Device state of one attention layer and the calls that drive it.
+
+`Layer` owns the HBM side of the look-ahead decode step for one layer: the
+resident slot pool, the block summaries, the per-KV-head block maps and the
+per-step outputs.  The full KV (records) lives elsewhere (pinned host memory
+or device memory) and is only read through `summarize`, `cold_fill` and
+`prefetch`.  Every method enqueues C-ABI calls on the current stream.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import lib
+from .configs import Config
+from .gen import TORCH_DTYPE
+
+
+class Layer:
+    def __init__(self, cfg: Config, ctx: np.ndarray, nbmax: int, device="cuda"):
+        self.cfg = cfg
+        self.shape = lib.Shape.of(cfg, nbmax)
+        B, H, K, d, Hq = cfg.batch, cfg.n_kv_heads, cfg.k_resident, cfg.head_dim, cfg.n_q_heads
+        dt = TORCH_DTYPE[cfg.dtype]
+        self.device = device
+        self.nbmax = nbmax
+        self.ctx_len = torch.as_tensor(np.asarray(ctx, np.int32), device=device)
+        self.pool = torch.zeros((B, H, K, cfg.record_elems), dtype=dt, device=device)
+        self.summ = torch.zeros((B, H, nbmax, 2, d), dtype=dt, device=device)
+        self.l2p = torch.full((B, H, nbmax), -1, dtype=torch.int32, device=device)
+        self.p2l = torch.full((B, H, K), -1, dtype=torch.int32, device=device)
+        self.last_sel = torch.zeros((B, H, K), dtype=torch.int32, device=device)
+        self.out = torch.zeros((B, 2, Hq, d), dtype=dt, device=device)
+        self.topk_idx = torch.full((B, H, K), -1, dtype=torch.int32, device=device)
+        self.topk_score = torch.zeros((B, H, K), dtype=torch.float32, device=device)
+        self.admit = torch.full((B, H, K, 3), -1, dtype=torch.int32, device=device)
+        self.admit_count = torch.zeros((B, H), dtype=torch.int32, device=device)
+
+    # ------------------------------------------------------------------ setup
+    def summarize(self, records):
+        lib.summarize(self.shape, records, self.ctx_len, self.summ)
+
+    def cold_fill(self, q: torch.Tensor, records, mode: int = lib.GATHER, host_staging=None):
+        """Initial resident set: the top-K blocks of the normal query's scores,
+        stamped 0, copied in from `records`."""
+        K = self.shape.k_resident
+        self.l2p.fill_(-1)
+        self.p2l.fill_(-1)
+        self.last_sel.zero_()
+        lib.score_topk(self.shape, q, self.summ, self.ctx_len, self.topk_idx, self.topk_score, q_row=0)
+        lib.capped_evict(self.shape, self.topk_idx, 0, K, self.l2p, self.p2l, self.last_sel,
+                         self.admit, self.admit_count)
+        self.prefetch(records, K, mode=mode, host_staging=host_staging)
+
+    def set_state(self, l2p, p2l, last_sel):
+        self.l2p.copy_(torch.as_tensor(l2p))
+        self.p2l.copy_(torch.as_tensor(p2l))
+        self.last_sel.copy_(torch.as_tensor(last_sel))
+
+    def state(self):
+        return (self.l2p.clone(), self.p2l.clone(), self.last_sel.clone())
+
+    # ------------------------------------------------------------------ per step
+    def step(self, q: torch.Tensor, step: int, max_admit: Optional[int] = None, scale: float = 0.0):
+        """Fused look-ahead layer step (attention, scan, top-K, eviction)."""
+        m = self.cfg.max_admit() if max_admit is None else max_admit
+        lib.layer_step(self.shape, q, self.pool, self.summ, self.ctx_len, step, m, self.out,
+                       self.topk_idx, self.topk_score, self.l2p, self.p2l, self.last_sel,
+                       self.admit, self.admit_count, scale=scale)
+
+    def step_unfused(self, q: torch.Tensor, step: int, max_admit: Optional[int] = None,
+                     scale: float = 0.0):
+        """The same step as four separate C-ABI calls."""
+        m = self.cfg.max_admit() if max_admit is None else max_admit
+        lib.lookahead_attn(self.shape, q, self.pool, self.p2l, self.ctx_len, self.out, scale=scale)
+        lib.score_topk(self.shape, q, self.summ, self.ctx_len, self.topk_idx, self.topk_score, q_row=1)
+        lib.capped_evict(self.shape, self.topk_idx, step, m, self.l2p, self.p2l, self.last_sel,
+                         self.admit, self.admit_count)
+
+    def prefetch(self, records, max_admit: Optional[int] = None, mode: int = lib.GATHER,
+                 host_staging=None, side_stream=None, wait_before=None, done=None):
+        m = self.cfg.max_admit() if max_admit is None else max_admit
+        lib.prefetch(self.shape, records, self.pool, self.admit, self.admit_count, m, mode=mode,
+                     host_staging=host_staging, side_stream=side_stream,
+                     wait_before=wait_before, done=done)

@@ -1,0 +1,427 @@
+"""GPU parity: every C-ABI call against the CPU oracle on seeded inputs.
+
+Small shapes are compared element by element; the full-size workloads are
+compared on sampled units (each sampled (request, KV head) pair is cut out as a
+one-request, one-KV-head problem for the oracle, which is exact because every
+step of the method is local to its unit).
+
+Tolerances: maps, admissions and summaries bit-exact (summaries by value);
+top-K exact except swaps within 1e-5 relative of the K-th score (and exact on
+small-integer inputs, where every score is exact in fp32); attention within
+1e-2 (bf16) or 1e-5 (fp32) absolute + relative of the fp64 oracle.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (ATTN_TOL, check_attention, check_topk, host, i32, pool_from_records,
+                    sample_units, unit_slice)
+from sparse_kv_block_amd import gen
+from sparse_kv_block_amd.configs import AGENTIC, GQA16, QWEN3_8B_16K, TINY, Config
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from sparse_kv_block_amd import lib            # noqa: E402  (fails loudly if not built)
+from sparse_kv_block_amd.pipeline import Layer  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(**kw) -> Config:
+    base = dict(name="small", dtype="bf16", batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                block_size=16, ctx=1000, k_resident=16, cap=0.25, draft_sigma=0.2, rho=0.95,
+                planted=4, seed=101)
+    base.update(kw)
+    return Config(**base)
+
+
+def setup(cfg: Config, ctx=None, seed=0, integer=False, device=DEV, nbmax=None):
+    ctx = gen.context_lengths(cfg) if ctx is None else np.asarray(ctx, np.int32)
+    nbmax = nbmax or max(1, cfg.max_blocks(int(max(ctx.max(), 1))))
+    if integer:
+        rec, q = gen.integer_inputs(cfg, ctx, nbmax, seed, device=device)
+    else:
+        qs = gen.query_sequence(cfg, 2, seed=cfg.seed + seed, device=device)
+        q = gen.step_queries(cfg, qs, 1, seed=cfg.seed + seed)
+        dirs = gen.planted_directions(cfg, qs[1]) if cfg.planted else None
+        rec = gen.records(cfg, ctx, nbmax, seed=cfg.seed + seed, device=device, planted_dir=dirs)
+    return ctx, nbmax, rec, q
+
+
+SMALL_CASES = [
+    dict(dtype="f32", head_dim=64, n_q_heads=4, n_kv_heads=2, k_resident=8, batch=1, ctx=1024),
+    dict(dtype="bf16", head_dim=128),
+    dict(dtype="bf16", head_dim=64, n_q_heads=4, n_kv_heads=4),
+    dict(dtype="bf16", head_dim=128, n_q_heads=32, n_kv_heads=2, k_resident=24),     # G = 16
+    dict(dtype="f32", head_dim=128, n_q_heads=6, n_kv_heads=2, k_resident=40),
+]
+RAGGED = [1000, 17, 0]      # partial last block, one full block + 1 token, empty request
+
+
+def case_id(c):
+    return "-".join(f"{k}{v}" for k, v in c.items())
+
+
+# --------------------------------------------------------------------------- summaries
+@pytest.mark.parametrize("case", SMALL_CASES, ids=case_id)
+def test_summarize(case):
+    cfg = small(**case)
+    ctx = RAGGED[:cfg.batch] if cfg.batch > 1 else [cfg.ctx]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=1)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summ.fill_(7)                       # sentinel for entries that must stay untouched
+    init = host(layer.summ).copy()
+    layer.summarize(rec)
+    got = oracle.to_f64(host(layer.summ))
+    ref = oracle.to_f64(oracle.summarize(rec.cpu(), ctx, 16, summ=init))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_summarize_from_pinned_host_records():
+    cfg = small(batch=2)
+    ctx, nbmax, rec, q = setup(cfg, [1000, 333], seed=2, device="cpu")
+    pinned = rec.pin_memory()
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(pinned)
+    torch.cuda.synchronize()
+    ref = oracle.summarize(rec, ctx, 16)
+    np.testing.assert_array_equal(oracle.to_f64(host(layer.summ)), oracle.to_f64(ref))
+
+
+# --------------------------------------------------------------------------- scores + top-K
+@pytest.mark.parametrize("case", SMALL_CASES, ids=case_id)
+@pytest.mark.parametrize("q_row", [0, 1])
+def test_score_topk_gaussian(case, q_row):
+    cfg = small(**case)
+    ctx = RAGGED[:cfg.batch] if cfg.batch > 1 else [cfg.ctx]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=3)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score,
+                   q_row=q_row)
+    summ = oracle.summarize(rec.cpu(), ctx, 16)
+    sc = oracle.block_scores(q.cpu(), summ, ctx, 16, q_row=q_row)
+    idx, _ = oracle.topk(sc, ctx, 16, cfg.k_resident)
+    check_topk(i32(layer.topk_idx), host(layer.topk_score), idx, sc, what=cfg.name)
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=case_id)
+def test_score_topk_exact_on_integer_inputs(case):
+    # scores of small integers are exact in fp32: ties abound and the order
+    # (score desc, block asc) must agree bit for bit
+    cfg = small(**case)
+    ctx = RAGGED[:cfg.batch] if cfg.batch > 1 else [cfg.ctx]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=4, integer=True)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score)
+    summ = oracle.summarize(rec.cpu(), ctx, 16)
+    sc = oracle.block_scores(q.cpu(), summ, ctx, 16)
+    idx, val = oracle.topk(sc, ctx, 16, cfg.k_resident)
+    np.testing.assert_array_equal(i32(layer.topk_idx), idx)
+    np.testing.assert_array_equal(host(layer.topk_score).astype(np.float64), val)
+
+
+def test_topk_with_more_slots_than_blocks_and_large_context():
+    # K > NB_b for short requests; NBmax 8192 (a 128K context) for the long one
+    cfg = small(batch=3, k_resident=200, n_q_heads=4, n_kv_heads=1)
+    ctx, nbmax, rec, q = setup(cfg, [131072, 100, 3200], seed=5)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score)
+    summ = oracle.summarize(rec.cpu(), ctx, 16)
+    sc = oracle.block_scores(q.cpu(), summ, ctx, 16)
+    idx, _ = oracle.topk(sc, ctx, 16, cfg.k_resident)
+    check_topk(i32(layer.topk_idx), host(layer.topk_score), idx, sc, what="large")
+
+
+# --------------------------------------------------------------------------- eviction
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("K", [8, 128, 256])
+def test_capped_evict_bit_exact(seed, K):
+    cfg = small(batch=4, k_resident=K, ctx=K * 16 * 3, n_q_heads=8, n_kv_heads=2)
+    rng = np.random.default_rng(seed)
+    ctx = np.array([cfg.ctx, K * 8, 40, cfg.ctx], np.int32)   # the 3rd has fewer blocks than K
+    nbmax = cfg.max_blocks()
+    fill = [1.0, 0.6, 0.0, 0.3][seed % 4]
+    l2p, p2l, ls = [x.numpy() for x in gen.random_state(cfg, ctx, nbmax, seed, fill=fill,
+                                                            stamp_max=6)]
+    scores = rng.integers(-4, 5, size=(cfg.batch, cfg.n_kv_heads, nbmax)).astype(np.float64)
+    T, _ = oracle.topk(scores, ctx, 16, K)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.set_state(l2p, p2l, ls)
+    m = [0, 1, 6, K][seed]
+    lib.capped_evict(layer.shape, torch.from_numpy(T).to(DEV), 7, m, layer.l2p, layer.p2l,
+                     layer.last_sel, layer.admit, layer.admit_count)
+    l2p_o, p2l_o, ls_o = l2p.copy(), p2l.copy(), ls.copy()
+    admit, count = oracle.capped_evict(T, 7, m, l2p_o, p2l_o, ls_o)
+    np.testing.assert_array_equal(i32(layer.l2p), l2p_o)
+    np.testing.assert_array_equal(i32(layer.p2l), p2l_o)
+    np.testing.assert_array_equal(i32(layer.last_sel), ls_o)
+    np.testing.assert_array_equal(i32(layer.admit), admit)
+    np.testing.assert_array_equal(i32(layer.admit_count), count)
+
+
+# --------------------------------------------------------------------------- attention
+@pytest.mark.parametrize("case", SMALL_CASES, ids=case_id)
+@pytest.mark.parametrize("fill", [1.0, 0.5])
+def test_lookahead_attention(case, fill):
+    cfg = small(**case)
+    ctx = RAGGED[:cfg.batch] if cfg.batch > 1 else [cfg.ctx]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=6)
+    l2p, p2l, ls = gen.random_state(cfg, ctx, nbmax, 6, fill=fill)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.set_state(l2p, p2l, ls)
+    layer.pool.copy_(pool_from_records(rec, layer.p2l))
+    lib.lookahead_attn(layer.shape, q, layer.pool, layer.p2l, layer.ctx_len, layer.out)
+    ref = oracle.attention(q.cpu(), rec.cpu(), p2l, ctx, 16)
+    check_attention(layer.out, ref, cfg.dtype, cfg.name)
+
+
+def test_attention_scale_argument():
+    cfg = small(batch=2)
+    ctx, nbmax, rec, q = setup(cfg, [1000, 200], seed=7)
+    l2p, p2l, ls = gen.random_state(cfg, ctx, nbmax, 7)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.set_state(l2p, p2l, ls)
+    layer.pool.copy_(pool_from_records(rec, layer.p2l))
+    lib.lookahead_attn(layer.shape, q, layer.pool, layer.p2l, layer.ctx_len, layer.out, scale=0.3)
+    ref = oracle.attention(q.cpu(), rec.cpu(), p2l, ctx, 16, scale=0.3)
+    check_attention(layer.out, ref, "bf16")
+
+
+# --------------------------------------------------------------------------- prefetch
+@pytest.mark.parametrize("mode", ["gather", "memcpy"])
+@pytest.mark.parametrize("src", ["pinned", "device"])
+def test_prefetch(mode, src):
+    cfg = small(batch=3, k_resident=16)
+    ctx, nbmax, rec, q = setup(cfg, [1000, 500, 40], seed=8, device="cpu")
+    l2p, p2l, ls = [x.numpy() for x in gen.random_state(cfg, ctx, nbmax, 8, fill=0.7)]
+    scores = np.random.default_rng(8).normal(size=(cfg.batch, cfg.n_kv_heads, nbmax))
+    T, _ = oracle.topk(scores, ctx, 16, cfg.k_resident)
+    admit, count = oracle.capped_evict(T, 3, 5, l2p, p2l, ls)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.pool.fill_(3)
+    layer.admit.copy_(torch.from_numpy(admit))
+    layer.admit_count.copy_(torch.from_numpy(count))
+    records = rec.pin_memory() if src == "pinned" else rec.to(DEV)
+    side = torch.cuda.Stream()
+    before = torch.cuda.Event()
+    done = torch.cuda.Event()
+    before.record()
+    staging = torch.empty(cfg.batch * cfg.n_kv_heads * (3 * cfg.k_resident + 1), dtype=torch.int32,
+                          pin_memory=True)
+    layer.prefetch(records, 5, mode=lib.GATHER if mode == "gather" else lib.MEMCPY,
+                   host_staging=staging, side_stream=side, wait_before=before, done=done)
+    torch.cuda.current_stream().wait_event(done)
+    torch.cuda.synchronize()
+    ref = np.full(tuple(layer.pool.shape), 0, dtype=np.uint16)
+    ref[...] = host(torch.full_like(layer.pool, 3, device="cpu"))
+    oracle.prefetch(rec, ref, admit, count, 16)
+    np.testing.assert_array_equal(host(layer.pool), ref)
+
+
+# --------------------------------------------------------------------------- fused step
+@pytest.mark.parametrize("case", SMALL_CASES, ids=case_id)
+def test_fused_step_equals_separate_calls(case):
+    cfg = small(**case)
+    ctx = RAGGED[:cfg.batch] if cfg.batch > 1 else [cfg.ctx]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=9)
+    state = gen.random_state(cfg, ctx, nbmax, 9, fill=0.8, stamp_max=3)
+    a, b = Layer(cfg, ctx, nbmax), Layer(cfg, ctx, nbmax)
+    for L in (a, b):
+        L.summarize(rec)
+        L.set_state(*state)
+        L.pool.copy_(pool_from_records(rec, L.p2l))
+    a.step(q, 4)
+    b.step_unfused(q, 4)
+    torch.cuda.synchronize()
+    for name in ("out", "topk_idx", "topk_score", "l2p", "p2l", "last_sel", "admit", "admit_count"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def oracle_step(cfg, rec, q, ctx, state, step, m):
+    l2p, p2l, ls = [np.ascontiguousarray(x.numpy() if isinstance(x, torch.Tensor) else x,
+                                         dtype=np.int32).copy() for x in state]
+    summ = oracle.summarize(rec, ctx, 16)
+    out, idx, val, admit, count = oracle.layer_step(q, rec, summ, ctx, 16, cfg.k_resident, step, m,
+                                                    l2p, p2l, ls)
+    sc = oracle.block_scores(q, summ, ctx, 16)
+    return dict(out=out, idx=idx, scores=sc, l2p=l2p, p2l=p2l, ls=ls, admit=admit, count=count)
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=case_id)
+def test_fused_step_exact_on_integer_inputs(case):
+    cfg = small(**case)
+    ctx = RAGGED[:cfg.batch] if cfg.batch > 1 else [cfg.ctx]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=10, integer=True)
+    state = gen.random_state(cfg, ctx, nbmax, 10, fill=0.9, stamp_max=3)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    layer.set_state(*state)
+    layer.pool.copy_(pool_from_records(rec, layer.p2l))
+    m = cfg.max_admit()
+    layer.step(q, 5, m)
+    ref = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, state, 5, m)
+    check_attention(layer.out, ref["out"], cfg.dtype)
+    np.testing.assert_array_equal(i32(layer.topk_idx), ref["idx"])
+    for k in ("l2p", "p2l"):
+        np.testing.assert_array_equal(i32(getattr(layer, k)), ref[k])
+    np.testing.assert_array_equal(i32(layer.last_sel), ref["ls"])
+    np.testing.assert_array_equal(i32(layer.admit), ref["admit"])
+    np.testing.assert_array_equal(i32(layer.admit_count), ref["count"])
+
+
+# --------------------------------------------------------------------------- multi-step
+def run_steps(cfg, ctx, nbmax, rec, qseq, nsteps, units=None, what=""):
+    """Carries the resident sets over decode steps on the GPU (fused step +
+    gather prefetch) and on the oracle.  Maps must agree bit for bit on every
+    unit whose top-K list agrees; a unit whose list differs inside the
+    tolerance is set back to the oracle's state before the next step.
+    `units`: compare only these (b, h) pairs, each as its own oracle problem."""
+    G, m = cfg.group, cfg.max_admit()
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    q1 = gen.step_queries(cfg, qseq, 1)
+    layer.cold_fill(q1, rec)
+    rec_cpu = {}
+    if units is None:
+        units = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_kv_heads)]
+        whole = True
+    else:
+        whole = False
+    # oracle cold fill on its own summaries: the normal query's top-K into empty slots
+    ora = {}
+    for key in ([None] if whole else units):
+        b, h = key if key is not None else (0, 0)
+        if whole:
+            r = rec.cpu()
+            c = ctx
+        else:
+            r = unit_slice(rec, b, h, G, "unit").cpu()
+            c = unit_slice(ctx, b, h, G, "ctx")
+        qq = q1.cpu() if whole else unit_slice(q1, b, h, G, "q").cpu()
+        summ = oracle.summarize(r, c, 16)
+        sc = oracle.block_scores(qq, summ, c, 16, q_row=0)
+        idx, _ = oracle.topk(sc, c, 16, cfg.k_resident)
+        nb = r.shape[2]
+        Bn, Hn = r.shape[0], r.shape[1]
+        l2p = np.full((Bn, Hn, nb), -1, np.int32)
+        p2l = np.full((Bn, Hn, cfg.k_resident), -1, np.int32)
+        ls = np.zeros((Bn, Hn, cfg.k_resident), np.int32)
+        oracle.capped_evict(idx, 0, cfg.k_resident, l2p, p2l, ls)
+        ora[key] = dict(rec=r, ctx=c, summ=summ, l2p=l2p, p2l=p2l, ls=ls)
+    resyncs = 0
+
+    def resync(key, o):
+        nonlocal resyncs
+        resyncs += 1
+        sl = (slice(None),) * 3 if whole else (slice(key[0], key[0] + 1), slice(key[1], key[1] + 1))
+        layer.l2p[sl] = torch.from_numpy(o["l2p"]).to(DEV)
+        layer.p2l[sl] = torch.from_numpy(o["p2l"]).to(DEV)
+        layer.last_sel[sl] = torch.from_numpy(o["ls"]).to(DEV)
+        layer.pool[sl] = pool_from_records(rec[sl] if not whole else rec, layer.p2l[sl])
+
+    # the cold fill itself
+    torch.cuda.synchronize()
+    for key, o in ora.items():
+        sl = (slice(None),) * 3 if whole else (slice(key[0], key[0] + 1), slice(key[1], key[1] + 1))
+        if not (np.array_equal(i32(layer.p2l[sl]), o["p2l"]) and
+                np.array_equal(i32(layer.l2p[sl]), o["l2p"])):
+            resync(key, o)
+    for step in range(1, nsteps + 1):
+        q = gen.step_queries(cfg, qseq, step)
+        say(f"{what} step {step}")
+        layer.step(q, step, m)
+        layer.prefetch(rec, m)
+        torch.cuda.synchronize()
+        for key, o in ora.items():
+            b, h = key if key is not None else (None, None)
+            sl = (slice(None),) * 3 if whole else (slice(b, b + 1), slice(h, h + 1))
+            qq = q.cpu() if whole else unit_slice(q, b, h, G, "q").cpu()
+            out, idx, val, admit, count = oracle.layer_step(
+                qq, o["rec"], o["summ"], o["ctx"], 16, cfg.k_resident, step, m,
+                o["l2p"], o["p2l"], o["ls"])
+            sc = oracle.block_scores(qq, o["summ"], o["ctx"], 16)
+            gout = layer.out if whole else layer.out[b:b + 1, :, h * G:(h + 1) * G]
+            check_attention(gout, out, cfg.dtype, f"{what} step {step} unit {key}")
+            gidx = i32(layer.topk_idx[sl])
+            differ = check_topk(gidx, host(layer.topk_score[sl]), idx, sc,
+                                what=f"{what} step {step}")
+            if differ == 0:
+                np.testing.assert_array_equal(i32(layer.l2p[sl]), o["l2p"])
+                np.testing.assert_array_equal(i32(layer.p2l[sl]), o["p2l"])
+                np.testing.assert_array_equal(i32(layer.last_sel[sl]), o["ls"])
+                np.testing.assert_array_equal(i32(layer.admit[sl]), admit)
+                np.testing.assert_array_equal(i32(layer.admit_count[sl[:2]]), count)
+            else:
+                resync(key, o)
+    return resyncs
+
+
+def test_tiny_f32_config_multi_step():
+    cfg = TINY.scaled(steps=4)
+    ctx = gen.context_lengths(cfg)
+    nbmax = cfg.max_blocks()
+    qseq = gen.query_sequence(cfg, 6, device=DEV)
+    rec = gen.records(cfg, ctx, nbmax, device=DEV)
+    run_steps(cfg, ctx, nbmax, rec, qseq, 4, what="tiny")
+
+
+def test_agentic_shape_reduced_batch_32_steps():
+    # the long-context agentic shape (lognormal contexts, 8K-128K) on 3 requests,
+    # all units, 32 carried steps with AR(1) drift
+    cfg = AGENTIC.scaled(batch=3)
+    ctx = gen.context_lengths(cfg)
+    nbmax = cfg.max_blocks(int(ctx.max()))
+    say("agentic contexts", ctx.tolist())
+    qseq = gen.query_sequence(cfg, cfg.steps + 1, device=DEV)
+    rec = gen.records(cfg, ctx, nbmax, device=DEV)
+    resyncs = run_steps(cfg, ctx, nbmax, rec, qseq, cfg.steps, what="agentic-b3")
+    say("resyncs", resyncs)
+
+
+# --------------------------------------------------------------------------- full sizes
+def full_size_check(cfg: Config, n_units: int, steps: int):
+    ctx = gen.context_lengths(cfg)
+    nbmax = cfg.max_blocks(int(ctx.max()))
+    say(f"{cfg.name}: generating B={cfg.batch} NBmax={nbmax}")
+    qseq = gen.query_sequence(cfg, steps + 1, device=DEV)
+    dirs = gen.planted_directions(cfg, qseq[1]) if cfg.planted else None
+    rec = gen.records(cfg, ctx, nbmax, device=DEV, planted_dir=dirs)
+    units = sample_units(cfg.batch, cfg.n_kv_heads, n_units, cfg.seed)
+    say(f"{cfg.name}: units {units}")
+    resyncs = run_steps(cfg, ctx, nbmax, rec, qseq, steps, units=units, what=cfg.name)
+    say(f"{cfg.name}: resyncs {resyncs}")
+    # summaries of the sampled units
+    layer_summ = Layer(cfg, ctx, nbmax)
+    layer_summ.summarize(rec)
+    for (b, h) in units[:4]:
+        r = unit_slice(rec, b, h, cfg.group, "unit").cpu()
+        ref = oracle.summarize(r, unit_slice(ctx, b, h, cfg.group, "ctx"), 16)
+        np.testing.assert_array_equal(oracle.to_f64(host(layer_summ.summ[b:b + 1, h:h + 1])),
+                                      oracle.to_f64(ref))
+
+
+def test_full_size_qwen3_8b_16k():
+    full_size_check(QWEN3_8B_16K, 12, 2)
+
+
+def test_full_size_gqa16():
+    full_size_check(GQA16, 8, 2)
+
+
+def test_full_size_agentic():
+    full_size_check(AGENTIC, 8, 3)
