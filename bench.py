@@ -16,7 +16,6 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -57,15 +56,6 @@ def algorithmic_bytes(cfg, ctx: np.ndarray) -> dict:
                 total=kv + summ + q_out + maps + B * 4)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_kv_block_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".h", ".hip")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profile(algo_total: int):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel sources."""
@@ -73,35 +63,36 @@ def traffic_from_profile(algo_total: int):
         rec = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
+    from sparse_kv_block_amd.profiling import kernel_source_hash
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, ctx, records_host, qs_host, nunits: int):
-    """The fp64 oracle (as it stands) on a sample of units of the same step."""
+def cpu_baseline(cfg, ctx, records_host, qs_host, min_cpu_seconds: float):
+    """The fp64 oracle (as it stands) on the same step: whole layer steps over
+    all units, repeated until about `min_cpu_seconds` of CPU time is spent."""
     import oracle
     from sparse_kv_block_amd import gen
     B, H = cfg.batch, cfg.n_kv_heads
-    units = np.arange(0, B * H, max(1, (B * H) // nunits), dtype=np.int32)[:nunits]
     nb = cfg.max_blocks(int(ctx.max()))
     rec = oracle.as_np(records_host)
-    summ = np.zeros((B, H, nb, 2, cfg.head_dim), dtype=rec.dtype)
     nth = oracle.default_threads()
-    oracle.summarize(rec, ctx, cfg.block_size, summ=summ, units=units, nthreads=nth)
-    l2p, p2l, ls = [x.numpy().copy() for x in gen.random_state(cfg, ctx, nb, 77, stamp_max=1)]
+    summ = oracle.summarize(rec, ctx, cfg.block_size, nthreads=nth)
+    state = [x.numpy().copy() for x in gen.random_state(cfg, ctx, nb, 77, stamp_max=1)]
     q = oracle.as_np(qs_host)
-    used = min(nth, len(units))
-    t0 = time.perf_counter()
-    oracle.attention(q, rec, p2l, ctx, cfg.block_size, units=units, nthreads=nth)
-    sc = oracle.block_scores(q, summ, ctx, cfg.block_size, 1, units=units, nthreads=nth)
-    idx, _ = oracle.topk(sc, ctx, cfg.block_size, cfg.k_resident, units=units)
-    oracle.capped_evict(idx, 1, cfg.max_admit(), l2p, p2l, ls, units=units)
-    dt = time.perf_counter() - t0
-    frac = len(units) / (B * H)
-    return {"value": frac / dt, "unit": "layer-steps/s", "cores": used, "kind": "oracle",
-            "sample": f"{len(units)} of {B * H} (request, KV head) units of one layer step "
-                      f"(attention, scan, top-K, eviction) in {dt:.2f} s, scaled to the whole step"}
+    reps, spent = 0, 0.0
+    while spent * nth < min_cpu_seconds or reps == 0:
+        l2p, p2l, ls = [x.copy() for x in state]
+        t0 = time.perf_counter()
+        oracle.layer_step(q, rec, summ, ctx, cfg.block_size, cfg.k_resident, 1, cfg.max_admit(),
+                          l2p, p2l, ls, nthreads=nth)
+        spent += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps / spent, "unit": "layer-steps/s", "cores": min(nth, B * H),
+            "kind": "oracle",
+            "sample": f"{reps} whole layer steps ({B * H} units each: attention, scan, top-K, "
+                      f"eviction) in {spent:.2f} s wall on {nth} threads"}
 
 
 def main():
@@ -110,10 +101,14 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_8b_16k")
-    ap.add_argument("--cpu-units", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time (wall x threads) the oracle baseline runs for")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pcie", action="store_true")
     ap.add_argument("--query-sets", type=int, default=8)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the run, launch a plain elementwise copy of this many MiB "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the look-ahead step has "
@@ -239,10 +234,18 @@ def main():
             f"memcpy {res['memcpy']['GBps']} GB/s")
 
     if not args.no_cpu_baseline:
-        log(f"[bench] oracle baseline on {args.cpu_units} units ...")
-        result["cpu_baseline"] = cpu_baseline(cfg, ctx, rec_host, qs[0].cpu(), args.cpu_units)
+        log(f"[bench] oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, ctx, rec_host, qs[0].cpu(), args.cpu_seconds)
         log(f"[bench] oracle: {result['cpu_baseline']['value']:.3f} layer-steps/s on "
             f"{result['cpu_baseline']['cores']} threads")
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)       # a kernel name nothing else in the run uses
+        torch.cuda.synchronize()
+        result["copy_calib_bytes"] = n * 4
     print(json.dumps(result), flush=True)
 
 

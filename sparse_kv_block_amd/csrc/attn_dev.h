@@ -14,7 +14,7 @@
 // which is exactly the B operand layout of the 16x16x16 P.V step, so P never
 // leaves registers.  Softmax is online with a lazy rescale: the running max
 // only moves when a block's max exceeds it by more than 8 (in log2 units), so
-// unnormalised weights stay below 2^8.  The four waves' partial (max, sum, O)
+// unnormalised weights stay below 2^8 and the rescale factor is almost always 1.  The four waves' partial (max, sum, O)
 // are merged through LDS at the end.
 //
 // f32 path: plain VALU (one wave per query row); it serves the small fp32
@@ -92,8 +92,6 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
   }
 
   const uint16_t* unit_pool = pool + (size_t)unit * sh.K * REC;
-  bf16x8 kc[KS];
-  i16x4 vc[NT];
   auto load = [&](int slot, bf16x8* kr, i16x4* vr) {
     const uint16_t* rec = unit_pool + (size_t)slot * REC;
 #pragma unroll
@@ -103,22 +101,13 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
     for (int nt = 0; nt < NT; ++nt)
       vr[nt] = *reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g);
   };
-
-  if (todo) load(s0 + __builtin_ctzll(todo), kc, vc);
-  while (todo) {
-    const int sl = __builtin_ctzll(todo);
-    todo &= todo - 1;
-    const int nv = __builtin_amdgcn_readlane(nv_l, sl);
-    bf16x8 kn[KS];
-    i16x4 vn[NT];
-    if (todo) load(s0 + __builtin_ctzll(todo), kn, vn);
-
+  auto process = [&](const bf16x8* kr, const i16x4* vr, int nv) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[kk], qop[rt][kk], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qop[rt][kk], z, 0, 0, 0);
       float zz[4];
       float bm = -INFINITY;
 #pragma unroll
@@ -127,14 +116,14 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
         bm = fmaxf(bm, zz[i]);
       }
       bm = xrow_max(bm);
+      // f is 1 unless the block max exceeds the running max by more than 8;
+      // multiplying unconditionally keeps the accumulators in place.
       const bool need = bm > m_run[rt] + 8.0f;
-      if (ballot(need)) {
-        const float f = need ? exp2f(m_run[rt] - bm) : 1.0f;
-        if (need) m_run[rt] = bm;
-        l_run[rt] *= f;
+      const float f = need ? exp2f(m_run[rt] - bm) : 1.0f;
+      m_run[rt] = need ? bm : m_run[rt];
+      l_run[rt] *= f;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[rt][nt] *= f;
-      }
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] *= f;
       i16x4 pb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -144,14 +133,29 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vc[nt], pb, acc[rt][nt], 0, 0, 0);
+        acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt], pb, acc[rt][nt], 0, 0, 0);
     }
-    if (todo) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) kc[kk] = kn[kk];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) vc[nt] = vn[nt];
-    }
+  };
+  // Two register buffers alternate: while one block is processed the next
+  // one's loads are in flight.
+  auto pop = [&]() -> int {
+    if (!todo) return -1;
+    const int sl = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    return sl;
+  };
+  bf16x8 ka[KS], kb[KS];
+  i16x4 va[NT], vb[NT];
+  int sa = pop();
+  if (sa >= 0) load(s0 + sa, ka, va);
+  while (sa >= 0) {
+    const int sb = pop();
+    if (sb >= 0) load(s0 + sb, kb, vb);
+    process(ka, va, __builtin_amdgcn_readlane(nv_l, sa));
+    if (sb < 0) break;
+    sa = pop();
+    if (sa >= 0) load(s0 + sa, ka, va);
+    process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb));
   }
 
   // ---- merge the four waves ----

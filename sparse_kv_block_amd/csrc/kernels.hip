@@ -122,13 +122,13 @@ __device__ __forceinline__ SelectPtrs select_ptrs(char* smem, int NBmax, int K) 
 
 // Scan + select for one unit; leaves the sorted list in p.sel_idx (entries
 // past kk set to -1) and writes the top-K outputs.
-template <typename T, int D>
+template <typename T, int D, int U>
 __device__ __forceinline__ void select_unit(const Shape& sh, const T* q, int q_row, const T* summ,
                                             int unit, int L, int32_t* topk_idx, float* topk_score,
                                             const SelectPtrs& p) {
   const int b = unit / sh.H, h = unit % sh.H;
   const int nb = n_blocks(L, sh.NBmax);
-  scan_unit<T, D>(sh, q, q_row, summ + (size_t)unit * sh.NBmax * 2 * D, b, h, nb, p.keys);
+  scan_unit<T, D, U>(sh, q, q_row, summ + (size_t)unit * sh.NBmax * 2 * D, b, h, nb, p.keys);
   __syncthreads();
   const int kk = topk_unit(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
   for (int t = threadIdx.x; t < sh.K; t += kThreads) {
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T*
   extern __shared__ __align__(16) char smem[];
   const int unit = blockIdx.x;
   const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
-  select_unit<T, D>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
+  select_unit<T, D, 4>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
 }
 
 // ------------------------------------------------------------------ eviction
@@ -186,6 +186,20 @@ __global__ __launch_bounds__(kThreads) void prefetch_gather_kernel(int K, int NB
 }
 
 // ------------------------------------------------------------------ fused layer step
+// Every unit runs attention (the resident blocks) and the summary scan +
+// top-K; only the eviction must come after both (it rewrites the slot map that
+// attention reads).  Half of the workgroups scan first: their compute-only
+// top-K phase then overlaps other workgroups' HBM streaming instead of all
+// workgroups stalling the memory system at the same moment.  The selector
+// alternates between consecutive workgroups of one XCD (workgroups are dealt
+// round-robin over the 8 XCDs) and between the workgroups a CU receives.
+__device__ __forceinline__ bool scan_first(int unit) { return ((unit >> 3) ^ (unit >> 8)) & 1; }
+
+// Attention merge area, placed before the select area in LDS.
+__host__ __device__ constexpr int attn_region(int D, int RT) {
+  return (attn_lds_bytes(D, RT) + 15) & ~15;
+}
+
 template <int D, int RT>
 __global__ __launch_bounds__(kThreads) void layer_step_bf16_kernel(
     Shape sh, const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
@@ -197,10 +211,15 @@ __global__ __launch_bounds__(kThreads) void layer_step_bf16_kernel(
   const int unit = blockIdx.x;
   const int b = unit / sh.H, h = unit % sh.H;
   const int L = ctx[b];
-  attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale_log2, out, reinterpret_cast<float*>(smem));
+  const SelectPtrs p = select_ptrs(smem + attn_region(D, RT), sh.NBmax, sh.K);
+  if (scan_first(unit)) {
+    select_unit<uint16_t, D, 8>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+    attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale_log2, out, reinterpret_cast<float*>(smem));
+  } else {
+    attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale_log2, out, reinterpret_cast<float*>(smem));
+    select_unit<uint16_t, D, 8>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+  }
   __syncthreads();
-  const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
-  select_unit<uint16_t, D>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
   evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
              p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
              admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
@@ -217,10 +236,15 @@ __global__ __launch_bounds__(kThreads) void layer_step_f32_kernel(
   const int unit = blockIdx.x;
   const int b = unit / sh.H, h = unit % sh.H;
   const int L = ctx[b];
-  attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
-  __syncthreads();
   const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
-  select_unit<float, D>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+  if (scan_first(unit)) {
+    select_unit<float, D, 4>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+    attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
+  } else {
+    attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
+    select_unit<float, D, 4>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+  }
+  __syncthreads();
   evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
              p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
              admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
@@ -325,8 +349,7 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
   const size_t sel = SelectLds(sh.NBmax, sh.K).total;
   if (dtype == 1) {
     const int rt = rt_of(sh.G);
-    const size_t att = attn_lds_bytes(sh.d, rt);
-    const size_t lds = att > sel ? att : sel;
+    const size_t lds = attn_region(sh.d, rt) + sel;
     const float sl = sc * kLog2e;
 #define OASIS_STEP(D_, RT_)                                                                   \
   hipLaunchKernelGGL((layer_step_bf16_kernel<D_, RT_>), grid, dim3(kThreads), lds, st, sh,    \

@@ -63,12 +63,12 @@ struct Elem<float> {
 };
 
 // Writes keys[j] for j < nb.  summ_unit points at the unit's [NBmax][2][D].
-template <typename T, int D>
+// U = summary records in flight per 16-lane group (registers vs. bytes in flight).
+template <typename T, int D, int U>
 __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__ q, int q_row,
                                           const T* __restrict__ summ_unit, int b, int h, int nb,
                                           uint32_t* keys) {
   constexpr int CPL = D / 16;   // channels per lane
-  constexpr int U = 4;          // blocks in flight per lane group
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int lane = tid % kWave;
@@ -120,17 +120,8 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
 }
 
 // ---------------------------------------------------------------- top-K
-// Scratch (LDS ints): red[2][kWaves] + 4 extra.
-__device__ __forceinline__ int block_count(bool pred, int* red, int parity) {
-  const int w = threadIdx.x / kWave;
-  const uint64_t m = ballot(pred);
-  if (lane_id() == 0) red[parity * kWaves + w] = __popcll(m);
-  __syncthreads();
-  int c = 0;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) c += red[parity * kWaves + v];
-  return c;
-}
+// Scratch `red` (LDS ints): [2][kWaves][4] counts + one shared counter.
+constexpr int kRedInts = 2 * kWaves * 4 + 4;
 
 // Selects the min(K, nb) best keys; writes sel_idx[0..kk) / sel_key[0..kk) in
 // (key desc, index asc) order and returns kk.  cand_* are K-entry scratch.
@@ -141,27 +132,36 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
   const int w = tid / kWave;
   const int kk = K < nb ? K : nb;
   if (kk <= 0) return 0;
-  // 1. K-th largest key by MSB-first bisection: T = max{v : #{key >= v} >= kk}.
+  // 1. K-th largest key T = max{v : #{key >= v} >= kk}, two bits per round:
+  //    the three candidates of the next two bits are counted with ballots.
   uint32_t T = 0;
   int parity = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int cnt = 0;
+  for (int shift = 30; shift >= 0; shift -= 2) {
+    const uint32_t c1 = T | (1u << shift), c2 = T | (2u << shift), c3 = T | (3u << shift);
+    int n1 = 0, n2 = 0, n3 = 0;
     for (int base = 0; base < nb; base += kThreads) {
       const int j = base + tid;
-      const uint64_t m = ballot(j < nb && keys[j] >= cand);
-      cnt += __popcll(m);
+      const uint32_t k = j < nb ? keys[j] : 0u;
+      n1 += __popcll(ballot(k >= c1));
+      n2 += __popcll(ballot(k >= c2));
+      n3 += __popcll(ballot(k >= c3));
     }
-    if (lane_id() == 0) red[parity * kWaves + w] = cnt;
+    int* r = red + (parity * kWaves + w) * 4;
+    if (lane_id() == 0) { r[0] = n1; r[1] = n2; r[2] = n3; }
     __syncthreads();
-    int tot = 0;
+    int t1 = 0, t2 = 0, t3 = 0;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) tot += red[parity * kWaves + v];
-    if (tot >= kk) T = cand;
+    for (int v = 0; v < kWaves; ++v) {
+      const int* rv = red + (parity * kWaves + v) * 4;
+      t1 += rv[0];
+      t2 += rv[1];
+      t3 += rv[2];
+    }
+    T = t3 >= kk ? c3 : (t2 >= kk ? c2 : (t1 >= kk ? c1 : T));
     parity ^= 1;
   }
   // 2. compact: keys > T anywhere, then the lowest-index keys == T.
-  int* cnt_gt = red + 2 * kWaves;    // shared counter
+  int* cnt_gt = red + 2 * kWaves * 4;
   if (tid == 0) *cnt_gt = 0;
   __syncthreads();
   for (int base = 0; base < nb; base += kThreads) {
@@ -180,12 +180,12 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     const int j = base + tid;
     const bool eq = j < nb && keys[j] == T;
     const uint64_t m = ballot(eq);
-    if (lane_id() == 0) red[parity * kWaves + w] = __popcll(m);
+    if (lane_id() == 0) red[(parity * kWaves + w) * 4] = __popcll(m);
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
-      const int c = red[parity * kWaves + v];
+      const int c = red[(parity * kWaves + v) * 4];
       off += v < w ? c : 0;
       tot += c;
     }
@@ -197,16 +197,24 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     taken += tot;
     parity ^= 1;
   }
+  // pad to a multiple of 4 so the ranking can read four entries at a time
+  if (tid < ((kk + 3) & ~3) - kk) {
+    cand_key[kk + tid] = 0u;
+    cand_idx[kk + tid] = 0x7FFFFFFF;
+  }
   __syncthreads();
   // 3. rank the kk candidates by (key desc, index asc).
   if (tid < kk) {
     const uint32_t k = cand_key[tid];
     const int j = cand_idx[tid];
     int rank = 0;
-    for (int p = 0; p < kk; ++p) {
-      const uint32_t kp = cand_key[p];
-      const int jp = cand_idx[p];
-      rank += (kp > k) || (kp == k && jp < j);
+    const int kk4 = (kk + 3) >> 2;
+#pragma unroll 4
+    for (int p = 0; p < kk4; ++p) {
+      const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
+      const u32x4 jp = reinterpret_cast<const u32x4*>(cand_idx)[p];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rank += (kp[e] > k) || (kp[e] == k && (int)jp[e] < j);
     }
     sel_idx[rank] = j;
     sel_key[rank] = k;
@@ -222,7 +230,7 @@ struct EvictScratch {
   int* miss;       // [K]
   int* victim;     // [K]
   uint64_t* vkey;  // [K]
-  int* red;        // [2*kWaves + 4]
+  int* red;        // [kRedInts]
 };
 
 // T: the unit's top-K list in LDS or global memory ([K], -1 = unused entry).
@@ -278,9 +286,18 @@ __device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int s
   int a = max_admit < nM ? max_admit : nM;
   a = a < nV ? a : nV;
   a = a < 0 ? 0 : a;
+  if (tid < ((K + 1) & ~1) - K) x.vkey[K + tid] = ~0ull;   // pad to an even count
+  __syncthreads();
   if (elig) {
     int rank = 0;
-    for (int p = 0; p < K; ++p) rank += x.vkey[p] < key;
+    const int K2 = (K + 1) >> 1;
+#pragma unroll 4
+    for (int p = 0; p < K2; ++p) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(x.vkey)[p];
+      const uint64_t a0 = ((uint64_t)v[1] << 32) | v[0];
+      const uint64_t a1 = ((uint64_t)v[3] << 32) | v[2];
+      rank += (a0 < key) + (a1 < key);
+    }
     if (rank < a) x.victim[rank] = tid;
   }
   __syncthreads();
@@ -316,16 +333,16 @@ struct SelectLds {
     int o = 0;
     auto take = [&](int bytes) { int r = o; o += (bytes + 15) & ~15; return r; };
     keys = take(NBmax * 4);
-    cand_idx = take(K * 4);
-    cand_key = take(K * 4);
+    cand_idx = take((K + 4) * 4);
+    cand_key = take((K + 4) * 4);
     sel_idx = take(K * 4);
     sel_key = take(K * 4);
     p2l_s = take(K * 4);
     ls_s = take(K * 4);
     miss = take(K * 4);
     victim = take(K * 4);
-    vkey = take(K * 8);
-    red = take((2 * kWaves + 4) * 4);
+    vkey = take((K + 2) * 8);
+    red = take(kRedInts * 4);
     total = o;
   }
 };

@@ -1,0 +1,129 @@
+"""Turns rocprofv3 CSV output into the short summaries kept under profiles/.
+
+    python -m sparse_kv_block_amd.profiling stats DIR --cmd "..." --out profiles/X.txt
+    python -m sparse_kv_block_amd.profiling counters --fetch DIR1 --write DIR2 \
+        --kernel layer_step_bf16 --copy-kernel elementwise --copy-bytes N \
+        --cmd-fetch "..." --cmd-write "..." --out profiles/X.json
+
+`counters` scales the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
+what the same counters read for a plain copy kernel of known size, and records
+a hash of the HIP sources so that stale numbers can be recognised.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[-1]
+
+
+def _rows(path: str):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def stats(d: str, cmd: str, out: str, top: int = 12):
+    rows = _rows(_find(d, "kernel_stats.csv"))
+    rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}",
+             f"# kernel sources: {kernel_source_hash()}", "",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel"]
+    for r in rows[:top]:
+        name = r.get("Name") or r.get("KernelName") or "?"
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r.get('Percentage', 0)):8.2f}  {name[:110]}")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
+def _counter_per_dispatch(d: str, counter: str, substr: str):
+    rows = _rows(_find(d, "counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or substr not in r.get("Kernel_Name", ""):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} rows for kernels matching {substr!r} in {d}")
+    vals = list(per.values())
+    return statistics.median(vals), len(vals)
+
+
+def counters(fetch_dir, write_dir, kernel, copy_kernel, copy_bytes, cmd_fetch, cmd_write, out,
+             algorithmic_bytes=None):
+    f_k, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
+    f_c, _ = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", copy_kernel)
+    w_k, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    w_c, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", copy_kernel)
+    sf = copy_bytes / (f_c * 1024.0)
+    sw = copy_bytes / (w_c * 1024.0)
+    fetch_b = f_k * 1024.0 * sf
+    write_b = w_k * 1024.0 * sw
+    rec = {
+        "kernel": kernel, "source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k, "dispatches": [nf, nw],
+        "copy_kernel": copy_kernel, "copy_bytes": copy_bytes,
+        "copy_fetch_kib": f_c, "copy_write_kib": w_c,
+        "fetch_scale": sf, "write_scale": sw,
+        "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "algorithmic_bytes_per_launch": algorithmic_bytes,
+        "commands": [cmd_fetch, cmd_write],
+    }
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--copy-kernel", required=True)
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--cmd-fetch", required=True)
+    c.add_argument("--cmd-write", required=True)
+    c.add_argument("--algorithmic-bytes", type=int, default=None)
+    c.add_argument("--out", required=True)
+    a = ap.parse_args()
+    if a.what == "stats":
+        print(stats(a.dir, a.cmd, a.out))
+    else:
+        print(json.dumps(counters(a.fetch, a.write, a.kernel, a.copy_kernel, a.copy_bytes,
+                                  a.cmd_fetch, a.cmd_write, a.out, a.algorithmic_bytes), indent=1))
+
+
+if __name__ == "__main__":
+    main()
