@@ -95,6 +95,80 @@ def cpu_baseline(cfg, ctx, records_host, qs_host, min_cpu_seconds: float):
                       f"eviction) in {spent:.2f} s wall on {nth} threads"}
 
 
+def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
+    """The 36-layer decode step with the fetch-cap sweep: per layer the fused
+    step on the main stream and the gather prefetch of its admissions on a side
+    stream, layer-local events between them.  One host pool serves all layers
+    (36 per-layer 8 GiB pools would exceed the host memory of one box); each
+    layer has its own queries, resident pool and summaries in HBM."""
+    import torch
+    from sparse_kv_block_amd import gen, lib
+    from sparse_kv_block_amd.configs import FULL_36
+    from sparse_kv_block_amd.pipeline import Decoder
+    cfg = FULL_36
+    ctx = gen.context_lengths(cfg)
+    nbmax = cfg.max_blocks()
+    L = cfg.layers
+    dev = "cuda"
+    rec_bytes = 2 * cfg.block_size * cfg.head_dim * cfg.esize
+    dec = Decoder(cfg, ctx, nbmax, L, device=dev)
+    n_q = warmup + steps + 1
+    qs = []
+    for l in range(L):
+        seq = gen.query_sequence(cfg, n_q + 1, seed=1000 * 4 + l, device=dev)
+        qs.append([None] + [gen.step_queries(cfg, seq, t, seed=1000 * 4 + l) for t in range(1, n_q + 1)])
+    out = {"layers": L, "batch": cfg.batch, "ctx": int(ctx.max()), "k_resident": cfg.k_resident,
+           "host_pool": "one pinned pool shared by all layers", "caps": []}
+    main = torch.cuda.current_stream()
+    for cap in cfg.caps_sweep:
+        m = cfg.max_admit(cap)
+        dec.setup(rec_host, [qs[l][1] for l in range(L)], summ_from=src_layer)
+        torch.cuda.synchronize()
+        admitted = torch.zeros((), dtype=torch.int64, device=dev)
+        t = 0
+        for _ in range(warmup):
+            t += 1
+            dec.step(rec_host, [qs[l][t] for l in range(L)], t, m)
+        dec.drain()
+        torch.cuda.synchronize()
+        admitted.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        a.record(main)
+        for _ in range(steps):
+            t += 1
+            dec.step(rec_host, [qs[l][t] for l in range(L)], t, m)
+            for layer in dec.layers:
+                admitted += layer.admit_count.sum()
+        dec.drain()
+        b.record(main)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - h0) / steps
+        dev_s = a.elapsed_time(b) / 1e3 / steps
+        # the same steps without the host link: fused kernels only
+        c, d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c.record(main)
+        for _ in range(steps):
+            for l, layer in enumerate(dec.layers):
+                layer.step(qs[l][t], t + 1, 0)
+        d.record(main)
+        torch.cuda.synchronize()
+        comp_s = c.elapsed_time(d) / 1e3 / steps
+        moved = int(admitted.item()) * rec_bytes / steps
+        row = {"cap": cap, "max_admit": m, "bytes_per_step": moved,
+               "bytes_bound": cfg.batch * cfg.n_kv_heads * L * m * rec_bytes,
+               "step_ms": round(dev_s * 1e3, 3), "wall_ms": round(wall * 1e3, 3),
+               "compute_only_ms": round(comp_s * 1e3, 3),
+               "host_link_GBps": round(moved / dev_s / 1e9, 2),
+               "attention_path_tokens_per_s": round(cfg.batch / dev_s, 1)}
+        out["caps"].append(row)
+        log(f"[bench] 36 layers cap {cap} (m={m}): {moved / 1e9:.3f} GB/step, step {dev_s * 1e3:.2f} ms, "
+            f"fused kernels alone {comp_s * 1e3:.2f} ms")
+    del dec
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +180,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pcie", action="store_true")
     ap.add_argument("--query-sets", type=int, default=8)
+    ap.add_argument("--pipeline", action="store_true",
+                    help="also run the 36-layer decode step with the fetch-cap sweep")
+    ap.add_argument("--pipeline-steps", type=int, default=3)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, launch a plain elementwise copy of this many MiB "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -232,6 +309,9 @@ def main():
                           "pcie_inclusive_layer_steps_per_s": round(1.0 / (ms_per_step / 1e3 + best), 2)}
         log(f"[bench] prefetch {nbytes / 1e6:.1f} MB: gather {res['gather']['GBps']} GB/s, "
             f"memcpy {res['memcpy']['GBps']} GB/s")
+
+    if args.pipeline:
+        result["pipeline_36_layer"] = pipeline_leg(layer, rec_host, args.pipeline_steps, 2)
 
     if not args.no_cpu_baseline:
         log(f"[bench] oracle baseline ...")

@@ -164,3 +164,10 @@ def integer_inputs(cfg: Config, ctx: np.ndarray, nbmax: int, seed: int,
     q = torch.randint(lo, hi + 1, (B, 2, Hq, d), generator=g).to(torch.float32)
     rec = rec.reshape(B, H, nbmax, 2 * S * d).to(dt).to(device)
     return rec, q.to(dt).to(device)
+
+
+def integer_queries(cfg: Config, n: int, seed: int, lo: int = -3, hi: int = 3, device="cpu"):
+    """n independent small-integer query tensors [B][2][Hq][d] (storage dtype)."""
+    g = _gen("cpu", seed * 131 + 17)
+    q = torch.randint(lo, hi + 1, (n, cfg.batch, 2, cfg.n_q_heads, cfg.head_dim), generator=g)
+    return [x.to(TORCH_DTYPE[cfg.dtype]).to(device).contiguous() for x in q.to(torch.float32)]

@@ -196,12 +196,26 @@ def prefetch(shape: Shape, records, pool, admit, admit_count, max_admit: int, mo
                 or host_staging.dtype != I32 or host_staging.numel() < n):
             raise ValueError(f"MEMCPY mode needs a pinned int32 host_staging of >= {n} elements")
         stg = ctypes.c_void_p(host_staging.data_ptr())
-    ev = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+    side = torch.cuda.current_stream() if side_stream is None else side_stream
+    # torch creates an event's hipEvent_t only when torch first records it: an
+    # event torch never recorded has handle 0.  `wait_before` in that state
+    # has nothing to wait for; `done` is created here (recorded once on the
+    # side stream) so that the library can record it and waiters see it.
+    wait = None
+    if wait_before is not None and wait_before.cuda_event:
+        wait = ctypes.c_void_p(wait_before.cuda_event)
+    fin = None
+    if done is not None:
+        if not done.cuda_event:
+            done.record(side)
+        if not done.cuda_event:
+            raise RuntimeError("could not create the completion event")
+        fin = ctypes.c_void_p(done.cuda_event)
     _check(_lib.oasis_prefetch(
         ctypes.byref(shape), _any(records, "records", dt, U * shape.max_blocks * shape.record_elems()),
         _dev(pool, "pool", dt, U * K * shape.record_elems()), _dev(admit, "admit", I32, U * K * 3),
         _dev(admit_count, "admit_count", I32, U), int(max_admit), int(mode), stg,
-        _stream(side_stream), ev(wait_before), ev(done)))
+        _stream(side), wait, fin))
 
 
 def layer_step(shape: Shape, q, pool, summ, ctx_len, step: int, max_admit: int, out, topk_idx,

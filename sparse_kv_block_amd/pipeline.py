@@ -85,3 +85,72 @@ class Layer:
         lib.prefetch(self.shape, records, self.pool, self.admit, self.admit_count, m, mode=mode,
                      host_staging=host_staging, side_stream=side_stream,
                      wait_before=wait_before, done=done)
+
+
+class Decoder:
+    """Several layers stepped in order, the way a decode step runs them.
+
+    Per layer and step, on the caller's (main) stream: wait for this layer's
+    previous prefetch, run the fused look-ahead step, record `ev_sel`.  On the
+    side stream: wait for `ev_sel`, prefetch the admitted blocks, record
+    `ev_pf`.  The event after the fused step covers both the admission list
+    and the write-after-read hazard on the victim slots (attention of this
+    step read them); the event after the prefetch is the layer-local
+    synchronisation the next step waits on.  Prefetches of different layers
+    queue on the one side stream (the host link is one resource) and overlap
+    the main stream's later layers.
+
+    All layers may share one `records` array (the host pool) when host memory
+    cannot hold one per layer; their queries differ.
+    """
+
+    def __init__(self, cfg: Config, ctx: np.ndarray, nbmax: int, n_layers: int, device="cuda"):
+        self.cfg = cfg
+        self.layers = [Layer(cfg, ctx, nbmax, device) for _ in range(n_layers)]
+        self.side = torch.cuda.Stream(device=device)
+        self.ev_sel = [torch.cuda.Event() for _ in range(n_layers)]
+        self.ev_pf = [torch.cuda.Event() for _ in range(n_layers)]
+        self.pending = [False] * n_layers
+        self.staging = None
+
+    def setup(self, records, qs_first, summ_from: Optional[Layer] = None):
+        """Summaries (computed once from `records`, or copied from `summ_from`)
+        and the cold fill of every layer."""
+        for i, layer in enumerate(self.layers):
+            if summ_from is not None:
+                layer.summ.copy_(summ_from.summ)
+            elif i == 0:
+                layer.summarize(records)
+            else:
+                layer.summ.copy_(self.layers[0].summ)
+            layer.cold_fill(qs_first[i], records)
+        self.pending = [False] * len(self.layers)
+
+    def step(self, records, qs, step: int, max_admit: Optional[int] = None, mode: int = lib.GATHER,
+             before_prefetch=None):
+        """One decode step over all layers; qs[i] is layer i's query tensor.
+        `before_prefetch(i)` (optional) is enqueued on the side stream before
+        layer i's prefetch (tests use it to delay the side stream)."""
+        m = self.cfg.max_admit() if max_admit is None else max_admit
+        main = torch.cuda.current_stream()
+        if mode == lib.MEMCPY and self.staging is None:
+            n = self.layers[0].shape.units() * (3 * self.cfg.k_resident + 1)
+            self.staging = torch.empty(n, dtype=torch.int32, pin_memory=True)
+        for i, layer in enumerate(self.layers):
+            if self.pending[i]:
+                main.wait_event(self.ev_pf[i])
+            layer.step(qs[i], step, m)
+            self.ev_sel[i].record(main)
+            if before_prefetch is not None:
+                self.side.wait_event(self.ev_sel[i])
+                with torch.cuda.stream(self.side):
+                    before_prefetch(i)
+            layer.prefetch(records, m, mode=mode, host_staging=self.staging,
+                           side_stream=self.side, wait_before=self.ev_sel[i], done=self.ev_pf[i])
+            self.pending[i] = True
+
+    def drain(self):
+        main = torch.cuda.current_stream()
+        for i in range(len(self.layers)):
+            if self.pending[i]:
+                main.wait_event(self.ev_pf[i])
