@@ -7,7 +7,8 @@
 // bf16 path: CDNA4 MFMA.  Each wave owns a contiguous range of the unit's
 // slots and streams their 8 KiB block records straight from HBM into
 // registers (no LDS staging: the record layout already matches the operand
-// layout), one block ahead of the math:
+// layout, and nontemporal loads keep the once-read stream from churning the
+// caches), one block ahead of the math:
 //   logits  D[token][row] = K[token][:] . Q[row][:]   mfma 16x16x32 bf16, d/32 steps
 //   output  O[c][row]    += V^T[c][token] . P[token][row]  mfma 16x16x16 bf16, d/16 tiles
 // The 16x16 logit tile leaves lane (g, n) holding rows n, tokens 4g..4g+3,
@@ -96,10 +97,11 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
     const uint16_t* rec = unit_pool + (size_t)slot * REC;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
-      kr[kk] = *reinterpret_cast<const bf16x8*>(rec + n * D + 32 * kk + 8 * g);
+      kr[kk] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(rec + n * D + 32 * kk + 8 * g));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      vr[nt] = *reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g);
+      vr[nt] = __builtin_nontemporal_load(
+          reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g));
   };
   auto process = [&](const bf16x8* kr, const i16x4* vr, int nv) {
 #pragma unroll

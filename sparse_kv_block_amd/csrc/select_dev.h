@@ -10,8 +10,8 @@
 // instead of 2G.  Sixteen lanes share one 512-byte bf16 summary record (8
 // channels each, one 16-byte load of the min row and one of the max row) and
 // reduce with DPP inside their 16-lane row; a wave covers 4 blocks per load.
-// The scores of the unit's whole context stay in LDS as order-preserving
-// 32-bit keys.
+// Summary loads are nontemporal (read once per step).  The scores of the
+// unit's whole context stay in LDS as order-preserving 32-bit keys.
 //
 // Top-K: MSB-first radix bisection on the keys, counting with wave ballots
 // (popcount) and one LDS exchange per bit, finds the K-th largest key T; keys
@@ -38,7 +38,7 @@ struct Elem<uint16_t> {
   template <int N>
   __device__ static __forceinline__ void load(const uint16_t* p, float* v) {
     if constexpr (N == 8) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
     } else {

@@ -17,7 +17,7 @@ import torch
 from .configs import Config
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "liboasis.so")
+LIB_PATH = os.environ.get("OASIS_LIBRARY") or os.path.join(PKG, "liboasis.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 F32, BF16 = 0, 1
