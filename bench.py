@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL = "layer_step_bf16_kernel"
+KERNEL = "layer_step_kernel<bf16, d=128, 1 row tile>"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "layer_step_qwen3_8b_16k_counters.json")
 
 

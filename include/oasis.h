@@ -192,11 +192,22 @@ oasis_status oasis_prefetch(const oasis_shape* shape, const void* records,
                             int32_t mode, int32_t* host_staging,
                             void* side_stream, void* wait_before, void* done);
 
+/* Workspace bytes oasis_layer_step needs for a shape: 0 while
+ * max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K lists
+ * of the split summary scan and one counter per unit). */
+size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape);
+
 /* S1..S4 fused — one look-ahead layer step in one launch: attention of both
- * rows over the current resident set (written to out), then the draft
- * row's summary scan, top-K and capped eviction as above.  Results are
- * identical to oasis_lookahead_attn, oasis_score_topk(q_row = 1) and
- * oasis_capped_evict called in that order on one stream. */
+ * rows over the current resident set (written to out), then the draft row's
+ * summary scan, top-K and capped eviction as above.  Results are identical to
+ * oasis_lookahead_attn, oasis_score_topk(q_row = 1) and oasis_capped_evict
+ * called in that order on one stream.  Contexts longer than 1024 blocks split
+ * the scan of a unit over several workgroups that meet in `workspace`
+ * (device memory, 256-byte aligned, at least
+ * oasis_layer_step_workspace_bytes(shape) bytes; NULL allowed when that is
+ * 0).  The caller zero-fills the workspace once before its first use; every
+ * call leaves it ready for the next.  Calls that may run concurrently need
+ * separate workspaces. */
 oasis_status oasis_layer_step(const oasis_shape* shape, const void* q,
                               const void* pool, const void* summ,
                               const int32_t* ctx_len, float scale,
@@ -204,6 +215,7 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q,
                               int32_t* topk_idx, float* topk_score,
                               int32_t* l2p, int32_t* p2l, int32_t* last_sel,
                               int32_t* admit, int32_t* admit_count,
+                              void* workspace, size_t workspace_bytes,
                               void* stream);
 
 #ifdef __cplusplus

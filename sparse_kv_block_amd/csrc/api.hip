@@ -86,7 +86,7 @@ size_t esize(const oasis_shape* s) { return s->dtype == OASIS_DTYPE_F32 ? 4 : 2;
 
 extern "C" {
 
-int32_t oasis_abi_version(void) { return 1; }
+int32_t oasis_abi_version(void) { return 2; }
 
 const char* oasis_last_error(void) { return g_error.c_str(); }
 
@@ -253,11 +253,20 @@ oasis_status oasis_prefetch(const oasis_shape* shape, const void* records, void*
   return OASIS_OK;
 }
 
+size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape) {
+  if (!shape || shape->n_kv_heads <= 0 || shape->batch <= 0 || shape->max_blocks <= 0 ||
+      shape->k_resident <= 0)
+    return 0;
+  return oasis::step_workspace_bytes(shape->batch * shape->n_kv_heads,
+                                     oasis::step_parts(shape->max_blocks), shape->k_resident);
+}
+
 oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const void* pool,
                               const void* summ, const int32_t* ctx_len, float scale, int32_t step,
                               int32_t max_admit, void* out, int32_t* topk_idx, float* topk_score,
                               int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
-                              int32_t* admit_count, void* stream) {
+                              int32_t* admit_count, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   const char* fn = "oasis_layer_step";
   if (oasis_status st = check_shape(shape, fn)) return st;
   if (max_admit < 0) return fail(OASIS_ERR_INVALID, "%s: max_admit %d < 0", fn, max_admit);
@@ -275,9 +284,19 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const voi
   OASIS_NONNULL(last_sel, fn);
   OASIS_NONNULL(admit, fn);
   OASIS_NONNULL(admit_count, fn);
+  const size_t need = oasis_layer_step_workspace_bytes(shape);
+  if (need > 0) {
+    OASIS_NONNULL(workspace, fn);
+    if (workspace_bytes < need)
+      return fail(OASIS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                  need);
+    if (((uintptr_t)workspace & 255) != 0)
+      return fail(OASIS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+  }
   return hip_status(oasis::launch_layer_step(to_shape(shape), shape->dtype, q, pool, summ, ctx_len,
                                              scale, step, max_admit, out, topk_idx, topk_score, l2p,
-                                             p2l, last_sel, admit, admit_count, (hipStream_t)stream),
+                                             p2l, last_sel, admit, admit_count,
+                                             need > 0 ? workspace : nullptr, (hipStream_t)stream),
                     fn);
 }
 

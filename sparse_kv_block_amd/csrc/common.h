@@ -97,4 +97,45 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// ---- split summary scan of long contexts (fused layer step) ----
+constexpr int kScanChunk = 2048;   // blocks per scan part
+
+struct StepWorkspace {
+  int32_t* counter;   // [units]         parts finished (reset to 0 by the last one)
+  int32_t* n;         // [units][parts]  length of each part's list
+  uint32_t* key;      // [units][parts][K]
+  int32_t* idx;       // [units][parts][K]
+};
+
+// Workgroups per unit of the fused step: one when the whole context fits one
+// scan part; otherwise one for the attention plus one per scan part.
+__host__ __device__ inline int scan_parts(int nb) {
+  return nb > kScanChunk ? (nb + kScanChunk - 1) / kScanChunk : 1;
+}
+__host__ __device__ inline int step_parts(int NBmax) {
+  return NBmax > kScanChunk ? 1 + scan_parts(NBmax) : 1;
+}
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline size_t step_workspace_bytes(int units, int parts, int K) {
+  if (parts <= 1) return 0;
+  return align256((size_t)units * 4) + align256((size_t)units * parts * 4) +
+         2 * align256((size_t)units * parts * K * 4);
+}
+
+__host__ __device__ inline StepWorkspace step_workspace(void* base, int units, int parts, int K) {
+  StepWorkspace w{nullptr, nullptr, nullptr, nullptr};
+  if (parts <= 1 || base == nullptr) return w;
+  char* p = static_cast<char*>(base);
+  w.counter = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)units * 4);
+  w.n = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)units * parts * 4);
+  w.key = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)units * parts * K * 4);
+  w.idx = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
 }  // namespace oasis

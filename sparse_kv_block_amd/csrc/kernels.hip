@@ -200,49 +200,107 @@ __host__ __device__ constexpr int attn_region(int D, int RT) {
   return (attn_lds_bytes(D, RT) + 15) & ~15;
 }
 
-template <int D, int RT>
-__global__ __launch_bounds__(kThreads) void layer_step_bf16_kernel(
-    Shape sh, const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
-    const uint16_t* __restrict__ summ, const int32_t* __restrict__ ctx, float scale_log2, int step,
-    int max_admit, uint16_t* __restrict__ out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
-    int32_t* admit_count) {
+// Long contexts (more than kScanChunk blocks) split a unit over several
+// workgroups: part 0 runs the attention, part p >= 1 scans blocks
+// [(p-1)*kScanChunk, p*kScanChunk) and selects its local top-K.  Each part
+// publishes its list (the attention part an empty one) to the workspace; the
+// part that finishes last (device-scope counter) concatenates the lists in part
+// order and selects the final top-K from them, then runs the eviction, which
+// therefore follows the unit's attention.  The concatenation keeps equal keys
+// in ascending block order (each list is sorted by (key desc, block asc) and
+// the parts cover ascending block ranges), so the result is the same as one
+// workgroup scanning the whole context.
+template <typename T, int D, int RT, int U>
+__global__ __launch_bounds__(kThreads) void layer_step_kernel(
+    Shape sh, const T* __restrict__ q, const T* __restrict__ pool, const T* __restrict__ summ,
+    const int32_t* __restrict__ ctx, float scale, int step, int max_admit, T* __restrict__ out,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l,
+    int32_t* last_sel, int32_t* admit, int32_t* admit_count, int parts, StepWorkspace ws) {
   extern __shared__ __align__(16) char smem[];
-  const int unit = blockIdx.x;
+  constexpr bool kMfma = sizeof(T) == 2;
+  const int units = sh.B * sh.H;
+  const int unit = blockIdx.x % units;
+  const int part = blockIdx.x / units;
   const int b = unit / sh.H, h = unit % sh.H;
   const int L = ctx[b];
-  const SelectPtrs p = select_ptrs(smem + attn_region(D, RT), sh.NBmax, sh.K);
-  if (scan_first(unit)) {
-    select_unit<uint16_t, D, 8>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
-    attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale_log2, out, reinterpret_cast<float*>(smem));
+  const int nb = n_blocks(L, sh.NBmax);
+  const int active = nb > kScanChunk ? 1 + scan_parts(nb) : 1;
+  if (part >= active) return;
+  const bool whole = active == 1;          // one workgroup does the whole unit
+  const int c0 = whole ? 0 : (part - 1) * kScanChunk;
+  const int len = whole ? nb : (nb - c0 < kScanChunk ? nb - c0 : kScanChunk);
+  const int tid = threadIdx.x;
+  const int attn_bytes = kMfma ? attn_region(D, RT) : 0;
+  const SelectPtrs p = select_ptrs(smem + attn_bytes, sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk,
+                                   sh.K);
+
+  auto attention = [&]() {
+    if constexpr (kMfma)
+      attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale, out, reinterpret_cast<float*>(smem));
+    else
+      attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
+  };
+  auto scan_select = [&]() -> int {
+    scan_unit<T, D, U>(sh, q, 1, summ + ((size_t)unit * sh.NBmax + c0) * 2 * D, b, h, len, p.keys);
+    __syncthreads();
+    return topk_unit(p.keys, len, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  };
+  int kk = 0;
+  if (!whole) {
+    if (part == 0) attention();
+    else kk = scan_select();
+  } else if (scan_first(unit)) {
+    kk = scan_select();
+    attention();
   } else {
-    attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale_log2, out, reinterpret_cast<float*>(smem));
-    select_unit<uint16_t, D, 8>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+    attention();
+    kk = scan_select();
+  }
+
+  if (!whole) {
+    const size_t slot = (size_t)unit * parts + part;
+    for (int t = tid; t < sh.K; t += kThreads) {
+      ws.key[slot * sh.K + t] = t < kk ? p.sel_key[t] : 0u;
+      ws.idx[slot * sh.K + t] = t < kk ? c0 + p.sel_idx[t] : -1;
+    }
+    if (tid == 0) ws.n[slot] = kk;
+    // Release: after the barrier every wave's stores are issued; one
+    // device-scope fence (an L2 write-back on gfx950, one per workgroup rather
+    // than one per wave) publishes them before the counter increment.
+    __syncthreads();
+    int* flag = p.ev.red + 2 * kWaves * 4 + 1;
+    if (tid == 0) {
+      __threadfence();
+      *flag = atomicAdd(ws.counter + unit, 1) == active - 1;
+      if (*flag) __threadfence();          // acquire the other parts' lists
+    }
+    __syncthreads();
+    if (!*flag) return;                    // another part finishes the unit
+    uint32_t* mkey = reinterpret_cast<uint32_t*>(smem + attn_bytes +
+                                                 SelectLds(sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk, sh.K).total);
+    int* midx = reinterpret_cast<int*>(mkey + parts * sh.K);
+    int total = 0;
+    for (int pp = 0; pp < active; ++pp) {
+      const size_t sl = (size_t)unit * parts + pp;
+      const int n = ws.n[sl];
+      for (int r = tid; r < n; r += kThreads) {
+        mkey[total + r] = ws.key[sl * sh.K + r];
+        midx[total + r] = ws.idx[sl * sh.K + r];
+      }
+      total += n;
+    }
+    __syncthreads();
+    kk = topk_unit(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+    for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
+    if (tid == 0) ws.counter[unit] = 0;    // ready for the next launch
+  } else {
+    for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] += c0;
   }
   __syncthreads();
-  evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
-             p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
-             admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void layer_step_f32_kernel(
-    Shape sh, const float* __restrict__ q, const float* __restrict__ pool,
-    const float* __restrict__ summ, const int32_t* __restrict__ ctx, float scale, int step,
-    int max_admit, float* __restrict__ out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
-    int32_t* admit_count) {
-  extern __shared__ __align__(16) char smem[];
-  const int unit = blockIdx.x;
-  const int b = unit / sh.H, h = unit % sh.H;
-  const int L = ctx[b];
-  const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
-  if (scan_first(unit)) {
-    select_unit<float, D, 4>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
-    attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
-  } else {
-    attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
-    select_unit<float, D, 4>(sh, q, 1, summ, unit, L, topk_idx, topk_score, p);
+  for (int t = tid; t < sh.K; t += kThreads) {
+    if (t >= kk) p.sel_idx[t] = -1;
+    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
+    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
   }
   __syncthreads();
   evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
@@ -253,6 +311,8 @@ __global__ __launch_bounds__(kThreads) void layer_step_f32_kernel(
 // ------------------------------------------------------------------ launchers
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
+
+constexpr size_t kMaxLds = 64 * 1024;   // dynamic LDS per workgroup
 
 float scale_or_default(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
 
@@ -343,28 +403,34 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
                              const void* summ, const int32_t* ctx, float scale, int step,
                              int max_admit, void* out, int32_t* topk_idx, float* topk_score,
                              int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
-                             int32_t* admit_count, hipStream_t st) {
+                             int32_t* admit_count, void* workspace, hipStream_t st) {
   const float sc = scale_or_default(scale, sh.d);
-  dim3 grid(sh.B * sh.H);
-  const size_t sel = SelectLds(sh.NBmax, sh.K).total;
+  const int parts = step_parts(sh.NBmax);
+  const StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
+  dim3 grid(sh.B * sh.H * parts);
+  const size_t sel = SelectLds(sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk, sh.K).total;
+  const size_t merge = parts > 1 ? (size_t)parts * sh.K * 8 : 0;
   if (dtype == 1) {
     const int rt = rt_of(sh.G);
-    const size_t lds = attn_region(sh.d, rt) + sel;
+    const size_t lds = attn_region(sh.d, rt) + sel + merge;
+    if (lds > kMaxLds) return hipErrorInvalidConfiguration;
     const float sl = sc * kLog2e;
-#define OASIS_STEP(D_, RT_)                                                                   \
-  hipLaunchKernelGGL((layer_step_bf16_kernel<D_, RT_>), grid, dim3(kThreads), lds, st, sh,    \
-                     (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ, ctx, sl, \
-                     step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l, last_sel, \
-                     admit, admit_count)
+#define OASIS_STEP(D_, RT_)                                                                     \
+  hipLaunchKernelGGL((layer_step_kernel<uint16_t, D_, RT_, 8>), grid, dim3(kThreads), lds, st, sh, \
+                     (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ, ctx, sl,   \
+                     step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l, last_sel,   \
+                     admit, admit_count, parts, ws)
     if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1); else OASIS_STEP(128, 2); }
     else             { if (rt == 1) OASIS_STEP(64, 1);  else OASIS_STEP(64, 2); }
 #undef OASIS_STEP
   } else {
-#define OASIS_STEP32(D_)                                                                      \
-  hipLaunchKernelGGL((layer_step_f32_kernel<D_>), grid, dim3(kThreads), sel, st, sh,          \
-                     (const float*)q, (const float*)pool, (const float*)summ, ctx, sc, step,  \
-                     max_admit, (float*)out, topk_idx, topk_score, l2p, p2l, last_sel, admit, \
-                     admit_count)
+    const size_t lds = sel + merge;
+    if (lds > kMaxLds) return hipErrorInvalidConfiguration;
+#define OASIS_STEP32(D_)                                                                        \
+  hipLaunchKernelGGL((layer_step_kernel<float, D_, 1, 4>), grid, dim3(kThreads), lds, st, sh,    \
+                     (const float*)q, (const float*)pool, (const float*)summ, ctx, sc, step,     \
+                     max_admit, (float*)out, topk_idx, topk_score, l2p, p2l, last_sel, admit,    \
+                     admit_count, parts, ws)
     if (sh.d == 128) OASIS_STEP32(128); else OASIS_STEP32(64);
 #undef OASIS_STEP32
   }

@@ -27,6 +27,6 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
                              const void* summ, const int32_t* ctx_len, float scale, int step,
                              int max_admit, void* out, int32_t* topk_idx, float* topk_score,
                              int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
-                             int32_t* admit_count, hipStream_t st);
+                             int32_t* admit_count, void* workspace, hipStream_t st);
 
 }  // namespace oasis

@@ -27,7 +27,8 @@ GATHER, MEMCPY = 0, 1
 SYMBOLS = ("oasis_abi_version", "oasis_last_error", "oasis_cap_to_max_admit",
            "oasis_record_bytes", "oasis_summary_bytes", "oasis_host_to_device_ptr",
            "oasis_summarize", "oasis_lookahead_attn", "oasis_score_topk",
-           "oasis_capped_evict", "oasis_prefetch", "oasis_layer_step")
+           "oasis_capped_evict", "oasis_prefetch", "oasis_layer_step",
+           "oasis_layer_step_workspace_bytes")
 
 
 class OasisError(RuntimeError):
@@ -77,7 +78,9 @@ def _load():
         "oasis_score_topk": ([SP, P, I32, P, P, P, P, P], I32),
         "oasis_capped_evict": ([SP, P, I32, I32, P, P, P, P, P, P], I32),
         "oasis_prefetch": ([SP, P, P, P, P, I32, I32, P, P, P, P], I32),
-        "oasis_layer_step": ([SP, P, P, P, P, F, I32, I32, P, P, P, P, P, P, P, P, P], I32),
+        "oasis_layer_step": ([SP, P, P, P, P, F, I32, I32, P, P, P, P, P, P, P, P, P,
+                              ctypes.c_size_t, P], I32),
+        "oasis_layer_step_workspace_bytes": ([SP], ctypes.c_size_t),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -218,8 +221,30 @@ def prefetch(shape: Shape, records, pool, admit, admit_count, max_admit: int, mo
         _stream(side), wait, fin))
 
 
+def _workspace(shape: Shape, ws):
+    need = layer_step_workspace_bytes(shape)
+    if need == 0:
+        return None, 0
+    if ws is None:
+        raise ValueError(f"this shape needs a {need}-byte layer-step workspace")
+    if ws.device.type != "cuda" or not ws.is_contiguous() or ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace must be a contiguous device tensor of >= {need} bytes")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def layer_step_workspace_bytes(shape: Shape) -> int:
+    return int(_lib.oasis_layer_step_workspace_bytes(ctypes.byref(shape)))
+
+
+def layer_step_workspace(shape: Shape, device="cuda"):
+    """A zero-filled workspace for layer_step (None when the shape needs none)."""
+    n = layer_step_workspace_bytes(shape)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
 def layer_step(shape: Shape, q, pool, summ, ctx_len, step: int, max_admit: int, out, topk_idx,
-               topk_score, l2p, p2l, last_sel, admit, admit_count, scale: float = 0.0, stream=None):
+               topk_score, l2p, p2l, last_sel, admit, admit_count, scale: float = 0.0, stream=None,
+               workspace=None):
     dt, U, K, d = shape.torch_dtype(), shape.units(), shape.k_resident, shape.head_dim
     qn = shape.batch * 2 * shape.n_q_heads * d
     _check(_lib.oasis_layer_step(
@@ -229,4 +254,4 @@ def layer_step(shape: Shape, q, pool, summ, ctx_len, step: int, max_admit: int, 
         _dev(topk_idx, "topk_idx", I32, U * K), _dev(topk_score, "topk_score", torch.float32, U * K),
         _dev(l2p, "l2p", I32, U * shape.max_blocks), _dev(p2l, "p2l", I32, U * K),
         _dev(last_sel, "last_sel", I32, U * K), _dev(admit, "admit", I32, U * K * 3),
-        _dev(admit_count, "admit_count", I32, U), _stream(stream)))
+        _dev(admit_count, "admit_count", I32, U), *_workspace(shape, workspace), _stream(stream)))

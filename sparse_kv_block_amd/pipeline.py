@@ -37,6 +37,7 @@ class Layer:
         self.topk_score = torch.zeros((B, H, K), dtype=torch.float32, device=device)
         self.admit = torch.full((B, H, K, 3), -1, dtype=torch.int32, device=device)
         self.admit_count = torch.zeros((B, H), dtype=torch.int32, device=device)
+        self.workspace = lib.layer_step_workspace(self.shape, device)
 
     # ------------------------------------------------------------------ setup
     def summarize(self, records):
@@ -68,7 +69,7 @@ class Layer:
         m = self.cfg.max_admit() if max_admit is None else max_admit
         lib.layer_step(self.shape, q, self.pool, self.summ, self.ctx_len, step, m, self.out,
                        self.topk_idx, self.topk_score, self.l2p, self.p2l, self.last_sel,
-                       self.admit, self.admit_count, scale=scale)
+                       self.admit, self.admit_count, scale=scale, workspace=self.workspace)
 
     def step_unfused(self, q: torch.Tensor, step: int, max_admit: Optional[int] = None,
                      scale: float = 0.0):

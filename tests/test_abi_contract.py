@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_helpers(L, ora):
     raw = L.raw()
-    assert raw.oasis_abi_version() == 1
+    assert raw.oasis_abi_version() == 2
     for cap, K in [(0.0, 128), (0.01, 128), (0.05, 128), (0.2, 128), (1.0, 128), (0.25, 8),
                    (2.0, 16), (-1.0, 8), (0.3, 10), (0.7, 10)]:
         assert L.cap_to_max_admit(cap, K) == ora.max_admit(cap, K), (cap, K)
@@ -71,7 +71,7 @@ def test_bad_shapes_are_rejected(L, kw, status):
     assert "oasis_summarize" in L.last_error()
     assert raw.oasis_score_topk(ctypes.byref(s), p, 1, p, p, p, p, None) == status
     assert raw.oasis_layer_step(ctypes.byref(s), p, p, p, p, 0.0, 1, 6, p, p, p, p, p, p, p, p,
-                                None) == status
+                                p, 1 << 30, None) == status
 
 
 def test_null_pointers_and_bad_scalars(L):
@@ -94,7 +94,28 @@ def test_empty_batch_is_a_no_op(L):
     raw = L.raw()
     s = shape(batch=0)
     assert raw.oasis_summarize(ctypes.byref(s), None, None, None, None) == L.OK
-    assert raw.oasis_layer_step(ctypes.byref(s), *([None] * 4), 0.0, 1, 6, *([None] * 8), None) == L.OK
+    assert raw.oasis_layer_step(ctypes.byref(s), *([None] * 4), 0.0, 1, 6, *([None] * 8), None, 0,
+                                None) == L.OK
+
+
+def test_layer_step_workspace_contract(L):
+    raw = L.raw()
+    short = shape(max_blocks=1024, k_resident=128, batch=4)
+    assert L.layer_step_workspace_bytes(short) == 0
+    long = shape(max_blocks=8192, k_resident=128, batch=64, n_kv_heads=8, n_q_heads=32)
+    need = L.layer_step_workspace_bytes(long)
+    parts, units = 1 + 8192 // 2048, 64 * 8          # attention part + 2048-block scan parts
+    assert need >= units * 4 + units * parts * 4 + 2 * units * parts * 128 * 4
+    assert need < 5 * 2**20
+    p = ctypes.c_void_p(4096)
+    args = [p] * 4 + [0.0, 1, 6] + [p] * 8
+    assert raw.oasis_layer_step(ctypes.byref(long), *args, None, need, None) == L.ERR_INVALID
+    assert "workspace is NULL" in L.last_error()
+    assert raw.oasis_layer_step(ctypes.byref(long), *args, p, need - 1, None) == L.ERR_INVALID
+    assert "needed" in L.last_error()
+    assert raw.oasis_layer_step(ctypes.byref(long), *args, ctypes.c_void_p(4096 + 16), need,
+                                None) == L.ERR_INVALID
+    assert "aligned" in L.last_error()
 
 
 def test_binding_refuses_cpu_tensors(L):

@@ -252,6 +252,30 @@ def test_fused_step_equals_separate_calls(case):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_step_split_scan_equals_separate_calls(dtype):
+    # contexts past 1024 blocks split the scan over several workgroups that
+    # merge their lists; the result must equal one workgroup's (separate calls)
+    cfg = small(dtype=dtype, batch=4, k_resident=128, n_q_heads=8, n_kv_heads=2, planted=0)
+    ctx = [131072, 40000, 16 * 1024 + 1, 900]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=12)
+    assert lib.layer_step_workspace_bytes(lib.Shape.of(cfg, nbmax)) > 0
+    state = gen.random_state(cfg, ctx, nbmax, 12, fill=0.9, stamp_max=3)
+    a, b = Layer(cfg, ctx, nbmax), Layer(cfg, ctx, nbmax)
+    for L in (a, b):
+        L.summarize(rec)
+        L.set_state(*state)
+        L.pool.copy_(pool_from_records(rec, L.p2l))
+    for step in (4, 5, 6):          # the workspace counters must reset between launches
+        a.step(q, step)
+        b.step_unfused(q, step)
+        torch.cuda.synchronize()
+        for name in ("out", "topk_idx", "topk_score", "l2p", "p2l", "last_sel", "admit",
+                     "admit_count"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (step, name)
+    assert int(a.workspace[:4 * cfg.batch * cfg.n_kv_heads].view(torch.int32).abs().sum()) == 0
+
+
 def oracle_step(cfg, rec, q, ctx, state, step, m):
     l2p, p2l, ls = [np.ascontiguousarray(x.numpy() if isinstance(x, torch.Tensor) else x,
                                          dtype=np.int32).copy() for x in state]
