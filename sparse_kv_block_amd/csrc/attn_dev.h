@@ -26,12 +26,18 @@
 
 namespace oasis {
 
-// LDS bytes the bf16 attention merge needs.
+// LDS bytes the bf16 attention merge needs (two [D][17] partial-output
+// buffers, per-wave row max and sum, per-row denominators).
 __host__ __device__ constexpr int attn_lds_bytes(int D, int RT) {
-  return (2 * RT * D * 17 + kWaves * 16 * RT * 2 + 16 * RT) * 4;
+  return (2 * D * 17 + kWaves * 16 * 2 + 16 * RT) * 4;
 }
-__host__ __device__ constexpr int attn_f32_lds_bytes() { return 0; }
 
+// RT = 16-row tiles of the stacked rows (1: up to 16 rows, 2: up to 32).
+// RT == 1: the four waves split the unit's slots four ways.
+// RT == 2: wave w takes row tile w & 1 and slot half w >> 1, so every wave
+// keeps one tile's accumulators; the two waves of a slot half read the same
+// records back to back (the second read is a cache hit), so those loads keep
+// the default cache policy instead of the streaming one.
 template <int D, int RT>
 __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
                                                const uint16_t* __restrict__ pool,
@@ -41,6 +47,7 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
   constexpr int KS = D / 32;   // logit MFMA steps
   constexpr int NT = D / 16;   // output tiles
   constexpr int REC = 2 * kBlock * D;
+  constexpr int NSPLIT = RT == 2 ? 2 : kWaves;
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int lane = tid % kWave;
@@ -48,11 +55,12 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
   const int n = lane & 15;
   const int G = sh.G;
   const int unit = b * sh.H + h;
+  const int rt = RT == 2 ? (w & 1) : 0;          // this wave's row tile
+  const int split = RT == 2 ? (w >> 1) : w;      // this wave's share of the slots
 
   // Query operand: lane (g, n) holds row 16*rt + n, channels 32*kk + 8g .. +8.
-  bf16x8 qop[RT][KS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  bf16x8 qop[KS];
+  {
     const int r = 16 * rt + n;
     const bool valid = r < 2 * G;
     const int row = r < G ? 0 : 1;
@@ -61,165 +69,159 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if (valid) {
-        qop[rt][kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
+        qop[kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
       } else {
         u32x4 z = {0u, 0u, 0u, 0u};
-        qop[rt][kk] = __builtin_bit_cast(bf16x8, z);
+        qop[kk] = __builtin_bit_cast(bf16x8, z);
       }
     }
   }
 
-  // This wave's slots and which of them hold a block with valid tokens.
-  const int s0 = (sh.K * w) / kWaves;
-  const int s1 = (sh.K * (w + 1)) / kWaves;
-  int j_l = -1, nv_l = 0;
-  if (lane < s1 - s0) {
-    j_l = p2l[(size_t)unit * sh.K + s0 + lane];
-    if (j_l >= 0 && j_l < sh.NBmax) {
-      int nv = L - j_l * kBlock;
-      nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
-    }
-  }
-  uint64_t todo = ballot(nv_l > 0);
-
-  float m_run[RT], l_run[RT];
-  f32x4 acc[RT][NT];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[NT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint16_t* unit_pool = pool + (size_t)unit * sh.K * REC;
   auto load = [&](int slot, bf16x8* kr, i16x4* vr) {
     const uint16_t* rec = unit_pool + (size_t)slot * REC;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      kr[kk] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(rec + n * D + 32 * kk + 8 * g));
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8* pk = reinterpret_cast<const bf16x8*>(rec + n * D + 32 * kk + 8 * g);
+      kr[kk] = RT == 1 ? __builtin_nontemporal_load(pk) : *pk;
+    }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      vr[nt] = __builtin_nontemporal_load(
-          reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g));
-  };
-  auto process = [&](const bf16x8* kr, const i16x4* vr, int nv) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qop[rt][kk], z, 0, 0, 0);
-      float zz[4];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        zz[i] = (4 * g + i < nv) ? z[i] * scale_log2 : -INFINITY;
-        bm = fmaxf(bm, zz[i]);
-      }
-      bm = xrow_max(bm);
-      // f is 1 unless the block max exceeds the running max by more than 8;
-      // multiplying unconditionally keeps the accumulators in place.
-      const bool need = bm > m_run[rt] + 8.0f;
-      const float f = need ? exp2f(m_run[rt] - bm) : 1.0f;
-      m_run[rt] = need ? bm : m_run[rt];
-      l_run[rt] *= f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] *= f;
-      i16x4 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t hb = f32_to_bf16_bits(exp2f(zz[i] - m_run[rt]));
-        pb[i] = (short)hb;
-        l_run[rt] += bf16_bits_to_f32(hb);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt], pb, acc[rt][nt], 0, 0, 0);
+    for (int nt = 0; nt < NT; ++nt) {
+      const i16x4* pv = reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g);
+      vr[nt] = RT == 1 ? __builtin_nontemporal_load(pv) : *pv;
     }
   };
-  // Two register buffers alternate: while one block is processed the next
-  // one's loads are in flight.
-  auto pop = [&]() -> int {
-    if (!todo) return -1;
-    const int sl = __builtin_ctzll(todo);
-    todo &= todo - 1;
-    return sl;
+  auto process = [&](const bf16x8* kr, const i16x4* vr, int nv) {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qop[kk], z, 0, 0, 0);
+    float zz[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      zz[i] = (4 * g + i < nv) ? z[i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, zz[i]);
+    }
+    bm = xrow_max(bm);
+    // f is 1 unless the block max exceeds the running max by more than 8;
+    // multiplying unconditionally keeps the accumulators in place.
+    const bool need = bm > m_run + 8.0f;
+    const float f = need ? exp2f(m_run - bm) : 1.0f;
+    m_run = need ? bm : m_run;
+    l_run *= f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] *= f;
+    i16x4 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t hb = f32_to_bf16_bits(exp2f(zz[i] - m_run));
+      pb[i] = (short)hb;
+      l_run += bf16_bits_to_f32(hb);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt], pb, acc[nt], 0, 0, 0);
   };
-  bf16x8 ka[KS], kb[KS];
-  i16x4 va[NT], vb[NT];
-  int sa = pop();
-  if (sa >= 0) load(s0 + sa, ka, va);
-  while (sa >= 0) {
-    const int sb = pop();
-    if (sb >= 0) load(s0 + sb, kb, vb);
-    process(ka, va, __builtin_amdgcn_readlane(nv_l, sa));
-    if (sb < 0) break;
-    sa = pop();
-    if (sa >= 0) load(s0 + sa, ka, va);
-    process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb));
+
+  // This wave's slots, 64 at a time; within a group two register buffers
+  // alternate: while one block is processed the next one's loads are in flight.
+  const int s0 = (sh.K * split) / NSPLIT;
+  const int s1 = (sh.K * (split + 1)) / NSPLIT;
+  for (int cb = s0; cb < s1; cb += kWave) {
+    int nv_l = 0;
+    if (lane < s1 - cb && lane < kWave) {
+      const int j = p2l[(size_t)unit * sh.K + cb + lane];
+      if (j >= 0 && j < sh.NBmax) {
+        const int nv = L - j * kBlock;
+        nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
+      }
+    }
+    uint64_t todo = ballot(nv_l > 0);
+    auto pop = [&]() -> int {
+      if (!todo) return -1;
+      const int sl = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      return sl;
+    };
+    bf16x8 ka[KS], kb[KS];
+    i16x4 va[NT], vb[NT];
+    int sa = pop();
+    if (sa >= 0) load(cb + sa, ka, va);
+    while (sa >= 0) {
+      const int sb = pop();
+      if (sb >= 0) load(cb + sb, kb, vb);
+      process(ka, va, __builtin_amdgcn_readlane(nv_l, sa));
+      if (sb < 0) break;
+      sa = pop();
+      if (sa >= 0) load(cb + sa, ka, va);
+      process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb));
+    }
   }
 
-  // ---- merge the four waves ----
-  float* obuf = lds;                                   // [2][RT][D][17]
-  float* mbuf = lds + 2 * RT * D * 17;                 // [kWaves][16*RT]
-  float* lbuf = mbuf + kWaves * 16 * RT;               // [kWaves][16*RT]
-  float* lstar = lbuf + kWaves * 16 * RT;              // [16*RT]
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const float lsum = xrow_sum(l_run[rt]);
+  // ---- merge the waves that share a row tile ----
+  float* obuf = lds;                                   // [2][D][17]
+  float* mbuf = lds + 2 * D * 17;                      // [kWaves][16]
+  float* lbuf = mbuf + kWaves * 16;                    // [kWaves][16]
+  float* lstar = lbuf + kWaves * 16;                   // [16*RT]
+  {
+    const float lsum = xrow_sum(l_run);
     if (g == 0) {
-      mbuf[w * 16 * RT + 16 * rt + n] = m_run[rt];
-      lbuf[w * 16 * RT + 16 * rt + n] = lsum;
+      mbuf[w * 16 + n] = m_run;
+      lbuf[w * 16 + n] = lsum;
     }
   }
   __syncthreads();
-  float fw[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + n;
+  float fw = 0.f;
+  {
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mbuf[v * 16 * RT + r]);
+    for (int v = 0; v < kWaves; ++v)
+      if (RT == 1 || (v & 1) == rt) M = fmaxf(M, mbuf[v * 16 + n]);
     float Ls = 0.f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
-      const float mv = mbuf[v * 16 * RT + r];
+      if (RT == 2 && (v & 1) != rt) continue;
+      const float mv = mbuf[v * 16 + n];
       const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
-      Ls += lbuf[v * 16 * RT + r] * f;
-      if (v == w) fw[rt] = f;
+      Ls += lbuf[v * 16 + n] * f;
+      if (v == w) fw = f;
     }
-    if (w == 0 && g == 0) lstar[r] = Ls;
+    if (w == rt && g == 0) lstar[16 * rt + n] = Ls;
   }
-  // waves 0,1 write their scaled partial outputs; waves 2,3 add theirs
+  // waves 0,1 write their scaled partial outputs into buffers 0,1; waves 2,3
+  // add theirs (RT == 1: both buffers hold rows 0..15; RT == 2: buffer t
+  // holds row tile t)
   for (int phase = 0; phase < 2; ++phase) {
     if ((w >> 1) == phase) {
-      float* ob = obuf + (w & 1) * RT * D * 17;
+      float* ob = obuf + (w & 1) * D * 17;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = 16 * nt + 4 * g + i;
-            float* p = ob + (rt * D + c) * 17 + n;
-            const float v = acc[rt][nt][i] * fw[rt];
-            if (phase == 0) *p = v; else *p += v;
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * nt + 4 * g + i;
+          float* p = ob + c * 17 + n;
+          const float v = acc[nt][i] * fw;
+          if (phase == 0) *p = v; else *p += v;
+        }
     }
     __syncthreads();
   }
   const int rows = 2 * G;
   for (int e = tid; e < rows * D; e += kThreads) {
     const int r = e / D, c = e % D;
-    const int rt = r / 16, rr = r % 16;
-    const float o0 = obuf[(rt * D + c) * 17 + rr];
-    const float o1 = obuf[RT * D * 17 + (rt * D + c) * 17 + rr];
+    const int rr = r % 16;
+    const float o = RT == 1 ? obuf[c * 17 + rr] + obuf[D * 17 + c * 17 + rr]
+                            : obuf[(r / 16) * D * 17 + c * 17 + rr];
     const float Ls = lstar[r];
-    const float o = Ls > 0.f ? (o0 + o1) / Ls : 0.f;
     const int row = r < G ? 0 : 1;
     const int head = h * G + (r < G ? r : r - G);
-    out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(o);
+    out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(Ls > 0.f ? o / Ls : 0.f);
   }
 }
 

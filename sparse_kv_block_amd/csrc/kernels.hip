@@ -415,13 +415,21 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     const size_t lds = attn_region(sh.d, rt) + sel + merge;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
     const float sl = sc * kLog2e;
-#define OASIS_STEP(D_, RT_)                                                                     \
-  hipLaunchKernelGGL((layer_step_kernel<uint16_t, D_, RT_, 8>), grid, dim3(kThreads), lds, st, sh, \
-                     (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ, ctx, sl,   \
-                     step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l, last_sel,   \
-                     admit, admit_count, parts, ws)
-    if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1); else OASIS_STEP(128, 2); }
-    else             { if (rt == 1) OASIS_STEP(64, 1);  else OASIS_STEP(64, 2); }
+    // One scan part per unit: unroll the scan 8 deep (more bytes in flight
+    // at 2 waves per SIMD).  Split scans: unroll 6, which fits 3 waves per
+    // SIMD, the better trade when many short workgroups share the CUs.
+#define OASIS_STEP(D_, RT_, U_)                                                                 \
+  hipLaunchKernelGGL((layer_step_kernel<uint16_t, D_, RT_, U_>), grid, dim3(kThreads), lds, st,  \
+                     sh, (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ, ctx,  \
+                     sl, step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l,        \
+                     last_sel, admit, admit_count, parts, ws)
+    if (parts == 1) {
+      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 8); else OASIS_STEP(128, 2, 8); }
+      else             { if (rt == 1) OASIS_STEP(64, 1, 8);  else OASIS_STEP(64, 2, 8); }
+    } else {
+      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 6); else OASIS_STEP(128, 2, 6); }
+      else             { if (rt == 1) OASIS_STEP(64, 1, 6);  else OASIS_STEP(64, 2, 6); }
+    }
 #undef OASIS_STEP
   } else {
     const size_t lds = sel + merge;
