@@ -39,28 +39,28 @@ __host__ __device__ constexpr int attn_lds_bytes(int D, int RT) {
 // records back to back (the second read is a cache hit), so those loads keep
 // the default cache policy instead of the streaming one.
 template <int D, int RT>
-__device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
-                                               const uint16_t* __restrict__ pool,
-                                               const int32_t* __restrict__ p2l, int b, int h,
-                                               int L, float scale_log2,
-                                               uint16_t* __restrict__ out, float* lds) {
-  constexpr int KS = D / 32;   // logit MFMA steps
-  constexpr int NT = D / 16;   // output tiles
-  constexpr int REC = 2 * kBlock * D;
-  constexpr int NSPLIT = RT == 2 ? 2 : kWaves;
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int lane = tid % kWave;
-  const int g = lane >> 4;
-  const int n = lane & 15;
-  const int G = sh.G;
-  const int unit = b * sh.H + h;
-  const int rt = RT == 2 ? (w & 1) : 0;          // this wave's row tile
-  const int split = RT == 2 ? (w >> 1) : w;      // this wave's share of the slots
+struct AttnWave {
+  static constexpr int KS = D / 32;   // logit MFMA steps
+  static constexpr int NT = D / 16;   // output tiles
+  static constexpr int REC = 2 * kBlock * D;
+  static constexpr int NSPLIT = RT == 2 ? 2 : kWaves;
 
-  // Query operand: lane (g, n) holds row 16*rt + n, channels 32*kk + 8g .. +8.
+  int w, g, n, rt, split;
   bf16x8 qop[KS];
-  {
+  float m_run, l_run;
+  f32x4 acc[NT];
+  const uint16_t* unit_pool;
+
+  __device__ __forceinline__ void init(const Shape& sh, const uint16_t* __restrict__ q,
+                                       const uint16_t* __restrict__ pool, int b, int h) {
+    const int lane = threadIdx.x % kWave;
+    w = threadIdx.x / kWave;
+    g = lane >> 4;
+    n = lane & 15;
+    rt = RT == 2 ? (w & 1) : 0;
+    split = RT == 2 ? (w >> 1) : w;
+    const int G = sh.G;
+    // query operand: lane (g, n) holds row 16*rt + n, channels 32*kk + 8g .. +8
     const int r = 16 * rt + n;
     const bool valid = r < 2 * G;
     const int row = r < G ? 0 : 1;
@@ -75,15 +75,33 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
         qop[kk] = __builtin_bit_cast(bf16x8, z);
       }
     }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    unit_pool = pool + (size_t)(b * sh.H + h) * sh.K * REC;
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // This wave's slot range.
+  __device__ __forceinline__ int slot_begin(const Shape& sh) const { return (sh.K * split) / NSPLIT; }
+  __device__ __forceinline__ int slot_end(const Shape& sh) const { return (sh.K * (split + 1)) / NSPLIT; }
 
-  const uint16_t* unit_pool = pool + (size_t)unit * sh.K * REC;
-  auto load = [&](int slot, bf16x8* kr, i16x4* vr) {
+  // Valid-token count of slot cb + lane (lanes past the range give 0).
+  __device__ __forceinline__ int slot_tokens(const Shape& sh, const int32_t* __restrict__ p2l, int unit,
+                                             int L, int cb, int ce) const {
+    const int lane = threadIdx.x % kWave;
+    int nv_l = 0;
+    if (lane < ce - cb) {
+      const int j = p2l[(size_t)unit * sh.K + cb + lane];
+      if (j >= 0 && j < sh.NBmax) {
+        const int nv = L - j * kBlock;
+        nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
+      }
+    }
+    return nv_l;
+  }
+
+  __device__ __forceinline__ void load(int slot, bf16x8* kr, i16x4* vr) const {
     const uint16_t* rec = unit_pool + (size_t)slot * REC;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -95,8 +113,9 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
       const i16x4* pv = reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g);
       vr[nt] = RT == 1 ? __builtin_nontemporal_load(pv) : *pv;
     }
-  };
-  auto process = [&](const bf16x8* kr, const i16x4* vr, int nv) {
+  }
+
+  __device__ __forceinline__ void process(const bf16x8* kr, const i16x4* vr, int nv, float scale_log2) {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
@@ -127,21 +146,89 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt], pb, acc[nt], 0, 0, 0);
-  };
+  }
 
-  // This wave's slots, 64 at a time; within a group two register buffers
-  // alternate: while one block is processed the next one's loads are in flight.
-  const int s0 = (sh.K * split) / NSPLIT;
-  const int s1 = (sh.K * (split + 1)) / NSPLIT;
-  for (int cb = s0; cb < s1; cb += kWave) {
-    int nv_l = 0;
-    if (lane < s1 - cb && lane < kWave) {
-      const int j = p2l[(size_t)unit * sh.K + cb + lane];
-      if (j >= 0 && j < sh.NBmax) {
-        const int nv = L - j * kBlock;
-        nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
+  // Merges the waves that share a row tile through LDS and writes the rows.
+  __device__ __forceinline__ void merge_store(const Shape& sh, int b, int h,
+                                              uint16_t* __restrict__ out, float* lds) const {
+    const int tid = threadIdx.x;
+    const int G = sh.G;
+    float* obuf = lds;                                   // [2][D][17]
+    float* mbuf = lds + 2 * D * 17;                      // [kWaves][16]
+    float* lbuf = mbuf + kWaves * 16;                    // [kWaves][16]
+    float* lstar = lbuf + kWaves * 16;                   // [16*RT]
+    {
+      const float lsum = xrow_sum(l_run);
+      if (g == 0) {
+        mbuf[w * 16 + n] = m_run;
+        lbuf[w * 16 + n] = lsum;
       }
     }
+    __syncthreads();
+    float fw = 0.f;
+    {
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v)
+        if (RT == 1 || (v & 1) == rt) M = fmaxf(M, mbuf[v * 16 + n]);
+      float Ls = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        if (RT == 2 && (v & 1) != rt) continue;
+        const float mv = mbuf[v * 16 + n];
+        const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
+        Ls += lbuf[v * 16 + n] * f;
+        if (v == w) fw = f;
+      }
+      if (w == rt && g == 0) lstar[16 * rt + n] = Ls;
+    }
+    // waves 0,1 write their scaled partial outputs into buffers 0,1; waves 2,3
+    // add theirs (RT == 1: both buffers hold rows 0..15; RT == 2: buffer t
+    // holds row tile t)
+    for (int phase = 0; phase < 2; ++phase) {
+      if ((w >> 1) == phase) {
+        float* ob = obuf + (w & 1) * D * 17;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 16 * nt + 4 * g + i;
+            float* p = ob + c * 17 + n;
+            const float v = acc[nt][i] * fw;
+            if (phase == 0) *p = v; else *p += v;
+          }
+      }
+      __syncthreads();
+    }
+    const int rows = 2 * G;
+    for (int e = tid; e < rows * D; e += kThreads) {
+      const int r = e / D, c = e % D;
+      const int rr = r % 16;
+      const float o = RT == 1 ? obuf[c * 17 + rr] + obuf[D * 17 + c * 17 + rr]
+                              : obuf[(r / 16) * D * 17 + c * 17 + rr];
+      const float Ls = lstar[r];
+      const int row = r < G ? 0 : 1;
+      const int head = h * G + (r < G ? r : r - G);
+      out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(Ls > 0.f ? o / Ls : 0.f);
+    }
+  }
+};
+
+template <int D, int RT>
+__device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
+                                               const uint16_t* __restrict__ pool,
+                                               const int32_t* __restrict__ p2l, int b, int h,
+                                               int L, float scale_log2,
+                                               uint16_t* __restrict__ out, float* lds) {
+  using AW = AttnWave<D, RT>;
+  AW a;
+  a.init(sh, q, pool, b, h);
+  const int unit = b * sh.H + h;
+  // This wave's slots, 64 at a time; within a group two register buffers
+  // alternate: while one block is processed the next one's loads are in flight.
+  const int s0 = a.slot_begin(sh), s1 = a.slot_end(sh);
+  for (int cb = s0; cb < s1; cb += kWave) {
+    const int nv_l = a.slot_tokens(sh, p2l, unit, L, cb, s1);
     uint64_t todo = ballot(nv_l > 0);
     auto pop = [&]() -> int {
       if (!todo) return -1;
@@ -149,80 +236,21 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
       todo &= todo - 1;
       return sl;
     };
-    bf16x8 ka[KS], kb[KS];
-    i16x4 va[NT], vb[NT];
+    bf16x8 ka[AW::KS], kb[AW::KS];
+    i16x4 va[AW::NT], vb[AW::NT];
     int sa = pop();
-    if (sa >= 0) load(cb + sa, ka, va);
+    if (sa >= 0) a.load(cb + sa, ka, va);
     while (sa >= 0) {
       const int sb = pop();
-      if (sb >= 0) load(cb + sb, kb, vb);
-      process(ka, va, __builtin_amdgcn_readlane(nv_l, sa));
+      if (sb >= 0) a.load(cb + sb, kb, vb);
+      a.process(ka, va, __builtin_amdgcn_readlane(nv_l, sa), scale_log2);
       if (sb < 0) break;
       sa = pop();
-      if (sa >= 0) load(cb + sa, ka, va);
-      process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb));
+      if (sa >= 0) a.load(cb + sa, ka, va);
+      a.process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb), scale_log2);
     }
   }
-
-  // ---- merge the waves that share a row tile ----
-  float* obuf = lds;                                   // [2][D][17]
-  float* mbuf = lds + 2 * D * 17;                      // [kWaves][16]
-  float* lbuf = mbuf + kWaves * 16;                    // [kWaves][16]
-  float* lstar = lbuf + kWaves * 16;                   // [16*RT]
-  {
-    const float lsum = xrow_sum(l_run);
-    if (g == 0) {
-      mbuf[w * 16 + n] = m_run;
-      lbuf[w * 16 + n] = lsum;
-    }
-  }
-  __syncthreads();
-  float fw = 0.f;
-  {
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-      if (RT == 1 || (v & 1) == rt) M = fmaxf(M, mbuf[v * 16 + n]);
-    float Ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      if (RT == 2 && (v & 1) != rt) continue;
-      const float mv = mbuf[v * 16 + n];
-      const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
-      Ls += lbuf[v * 16 + n] * f;
-      if (v == w) fw = f;
-    }
-    if (w == rt && g == 0) lstar[16 * rt + n] = Ls;
-  }
-  // waves 0,1 write their scaled partial outputs into buffers 0,1; waves 2,3
-  // add theirs (RT == 1: both buffers hold rows 0..15; RT == 2: buffer t
-  // holds row tile t)
-  for (int phase = 0; phase < 2; ++phase) {
-    if ((w >> 1) == phase) {
-      float* ob = obuf + (w & 1) * D * 17;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * nt + 4 * g + i;
-          float* p = ob + c * 17 + n;
-          const float v = acc[nt][i] * fw;
-          if (phase == 0) *p = v; else *p += v;
-        }
-    }
-    __syncthreads();
-  }
-  const int rows = 2 * G;
-  for (int e = tid; e < rows * D; e += kThreads) {
-    const int r = e / D, c = e % D;
-    const int rr = r % 16;
-    const float o = RT == 1 ? obuf[c * 17 + rr] + obuf[D * 17 + c * 17 + rr]
-                            : obuf[(r / 16) * D * 17 + c * 17 + rr];
-    const float Ls = lstar[r];
-    const int row = r < G ? 0 : 1;
-    const int head = h * G + (r < G ? r : r - G);
-    out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(Ls > 0.f ? o / Ls : 0.f);
-  }
+  a.merge_store(sh, b, h, out, lds);
 }
 
 // fp32 look-ahead attention: one wave per query row, 64 tokens (4 slots) per

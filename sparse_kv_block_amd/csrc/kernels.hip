@@ -8,6 +8,7 @@
 #include "attn_dev.h"
 #include "launch.h"
 #include "select_dev.h"
+#include "step_dev.h"
 
 namespace oasis {
 
@@ -210,7 +211,7 @@ __host__ __device__ constexpr int attn_region(int D, int RT) {
 // in ascending block order (each list is sorted by (key desc, block asc) and
 // the parts cover ascending block ranges), so the result is the same as one
 // workgroup scanning the whole context.
-template <typename T, int D, int RT, int U>
+template <typename T, int D, int RT, int U, bool IL>
 __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     Shape sh, const T* __restrict__ q, const T* __restrict__ pool, const T* __restrict__ summ,
     const int32_t* __restrict__ ctx, float scale, int step, int max_admit, T* __restrict__ out,
@@ -249,6 +250,15 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   if (!whole) {
     if (part == 0) attention();
     else kk = scan_select();
+  } else if (IL && kMfma && (RT == 1 || sh.K <= 128)) {
+    // one pass streams the unit's blocks and its summary records together
+    if constexpr (IL && kMfma) {
+      attn_scan_unit_bf16<D, RT, RT == 1 ? 2 : 1, 8>(
+          sh, q, pool, p2l, summ + (size_t)unit * sh.NBmax * 2 * D, nb, b, h, L, scale, out,
+          reinterpret_cast<float*>(smem), p.keys);
+      __syncthreads();
+      kk = topk_unit(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+    }
   } else if (scan_first(unit)) {
     kk = scan_select();
     attention();
@@ -415,27 +425,28 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     const size_t lds = attn_region(sh.d, rt) + sel + merge;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
     const float sl = sc * kLog2e;
-    // One scan part per unit: unroll the scan 8 deep (more bytes in flight
-    // at 2 waves per SIMD).  Split scans: unroll 6, which fits 3 waves per
-    // SIMD, the better trade when many short workgroups share the CUs.
-#define OASIS_STEP(D_, RT_, U_)                                                                 \
-  hipLaunchKernelGGL((layer_step_kernel<uint16_t, D_, RT_, U_>), grid, dim3(kThreads), lds, st,  \
-                     sh, (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ, ctx,  \
-                     sl, step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l,        \
+    // One scan part per unit: attention and scan interleaved in one pass (at
+    // 2 waves per SIMD).  Split scans: separate phases with a 6-deep scan
+    // unroll, which fits 3 waves per SIMD, the better trade when many short
+    // workgroups share the CUs.
+#define OASIS_STEP(D_, RT_, U_, IL_)                                                            \
+  hipLaunchKernelGGL((layer_step_kernel<uint16_t, D_, RT_, U_, IL_>), grid, dim3(kThreads), lds, \
+                     st, sh, (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ,   \
+                     ctx, sl, step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l,   \
                      last_sel, admit, admit_count, parts, ws)
     if (parts == 1) {
-      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 8); else OASIS_STEP(128, 2, 8); }
-      else             { if (rt == 1) OASIS_STEP(64, 1, 8);  else OASIS_STEP(64, 2, 8); }
+      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 8, true); else OASIS_STEP(128, 2, 8, true); }
+      else             { if (rt == 1) OASIS_STEP(64, 1, 8, true);  else OASIS_STEP(64, 2, 8, true); }
     } else {
-      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 6); else OASIS_STEP(128, 2, 6); }
-      else             { if (rt == 1) OASIS_STEP(64, 1, 6);  else OASIS_STEP(64, 2, 6); }
+      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 6, false); else OASIS_STEP(128, 2, 6, false); }
+      else             { if (rt == 1) OASIS_STEP(64, 1, 6, false);  else OASIS_STEP(64, 2, 6, false); }
     }
 #undef OASIS_STEP
   } else {
     const size_t lds = sel + merge;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
 #define OASIS_STEP32(D_)                                                                        \
-  hipLaunchKernelGGL((layer_step_kernel<float, D_, 1, 4>), grid, dim3(kThreads), lds, st, sh,    \
+  hipLaunchKernelGGL((layer_step_kernel<float, D_, 1, 4, false>), grid, dim3(kThreads), lds, st, sh,    \
                      (const float*)q, (const float*)pool, (const float*)summ, ctx, sc, step,     \
                      max_admit, (float*)out, topk_idx, topk_score, l2p, p2l, last_sel, admit,    \
                      admit_count, parts, ws)

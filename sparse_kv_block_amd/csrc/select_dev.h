@@ -62,8 +62,41 @@ struct Elem<float> {
   __device__ static __forceinline__ float one(const float* p) { return *p; }
 };
 
+// Halved group sums of the query row over the G query heads of KV head h, for
+// channels c0 .. c0+CPL: Qh = sum_i q_ic / 2, Ah = sum_i |q_ic| / 2.
+template <typename T, int D, int CPL>
+__device__ __forceinline__ void group_query_sums(const Shape& sh, const T* __restrict__ q,
+                                                 int q_row, int b, int h, int c0, float* Qh,
+                                                 float* Ah) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) { Qh[i] = 0.f; Ah[i] = 0.f; }
+  for (int i = 0; i < sh.G; ++i) {
+    float v[CPL];
+    Elem<T>::template load<CPL>(q + ((size_t)(b * 2 + q_row) * sh.Hq + h * sh.G + i) * D + c0, v);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) { Qh[c] += v[c]; Ah[c] += fabsf(v[c]); }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) { Qh[c] *= 0.5f; Ah[c] *= 0.5f; }
+}
+
+// This lane's part of one block's score (channels of its slice), in the
+// channel order every scan path uses, so all of them agree bit for bit.
+template <int CPL>
+__device__ __forceinline__ float record_part(const float* lo, const float* hi, const float* Qh,
+                                             const float* Ah) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    s = fmaf(lo[c] + hi[c], Qh[c], s);
+    s = fmaf(hi[c] - lo[c], Ah[c], s);
+  }
+  return s;
+}
+
 // Writes keys[j] for j < nb.  summ_unit points at the unit's [NBmax][2][D].
 // U = summary records in flight per 16-lane group (registers vs. bytes in flight).
+// Wave w scans the records 16t + 4w + quad (t = 0, 1, ...), quad = lane / 16.
 template <typename T, int D, int U>
 __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__ q, int q_row,
                                           const T* __restrict__ summ_unit, int b, int h, int nb,
@@ -77,16 +110,7 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
   const int c0 = n * CPL;
 
   float Qh[CPL], Ah[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) { Qh[i] = 0.f; Ah[i] = 0.f; }
-  for (int i = 0; i < sh.G; ++i) {
-    float v[CPL];
-    Elem<T>::template load<CPL>(q + ((size_t)(b * 2 + q_row) * sh.Hq + h * sh.G + i) * D + c0, v);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) { Qh[c] += v[c]; Ah[c] += fabsf(v[c]); }
-  }
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) { Qh[c] *= 0.5f; Ah[c] *= 0.5f; }
+  group_query_sums<T, D, CPL>(sh, q, q_row, b, h, c0, Qh, Ah);
 
   for (int jb = w * 4; jb < nb; jb += kThreads / 16 * U) {
     float part[U];
@@ -102,13 +126,7 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
 #pragma unroll
         for (int c = 0; c < CPL; ++c) { lo[c] = 0.f; hi[c] = 0.f; }
       }
-      float s = 0.f;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        s = fmaf(lo[c] + hi[c], Qh[c], s);
-        s = fmaf(hi[c] - lo[c], Ah[c], s);
-      }
-      part[u] = s;
+      part[u] = record_part<CPL>(lo, hi, Qh, Ah);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -1,0 +1,121 @@
+// One unit's attention and summary scan interleaved in a single pass per wave.
+//
+// Run back to back, the two phases of a unit leave the memory system idle at
+// every transition (and the top-K tail of every workgroup lands at the same
+// time).  Here each wave streams its attention blocks and its share of the
+// summary records together: every step processes one 8 KiB block record and
+// SG groups of four 512-byte summary records (SG * 2 KiB), with the next step's
+// loads in flight, so the workgroup streams its whole 1.5 MiB without a phase
+// change.  Groups left over once the wave's blocks are done go through a
+// deeper scan-only loop.  The per-block score arithmetic is the scan path's
+// (record_part, row16_sum), so the keys are bit-identical to oasis_score_topk's.
+#pragma once
+
+#include "attn_dev.h"
+#include "select_dev.h"
+
+namespace oasis {
+
+// Requires this wave's slot range to be at most 64 slots (K <= 256 with one
+// row tile, K <= 128 with two).  Writes keys[j] for j < nb and the attention
+// output; ends with the attention merge (so the keys are complete in LDS for
+// the whole workgroup afterwards).
+template <int D, int RT, int SG, int UL>
+__device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
+                                                    const uint16_t* __restrict__ pool,
+                                                    const int32_t* __restrict__ p2l,
+                                                    const uint16_t* __restrict__ summ_unit, int nb,
+                                                    int b, int h, int L, float scale_log2,
+                                                    uint16_t* __restrict__ out, float* lds,
+                                                    uint32_t* keys) {
+  using AW = AttnWave<D, RT>;
+  constexpr int CPL = D / 16;
+  constexpr int RW = CPL / 2;          // 32-bit words of one summary row slice
+  AW a;
+  a.init(sh, q, pool, b, h);
+  const int unit = b * sh.H + h;
+  const int w = a.w, quad = a.g, n = a.n;
+  const int c0 = n * CPL;
+  float Qh[CPL], Ah[CPL];
+  group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Qh, Ah);
+  const int Gw = nb > 4 * w ? (nb - 4 * w + 15) / 16 : 0;   // this wave's record groups
+
+  using Row = uint32_t __attribute__((ext_vector_type(RW)));
+  auto load_groups = [&](int t, int cnt, Row* lo, Row* hi) {
+#pragma unroll
+    for (int k = 0; k < cnt; ++k) {
+      const int j = 16 * (t + k) + 4 * w + quad;
+      if (t + k < Gw && j < nb) {
+        const uint16_t* rec = summ_unit + (size_t)j * 2 * D + c0;
+        lo[k] = __builtin_nontemporal_load(reinterpret_cast<const Row*>(rec));
+        hi[k] = __builtin_nontemporal_load(reinterpret_cast<const Row*>(rec + D));
+      } else {
+        lo[k] = Row(0u);
+        hi[k] = Row(0u);
+      }
+    }
+  };
+  auto score_groups = [&](int t, int cnt, const Row* lo, const Row* hi) {
+#pragma unroll
+    for (int k = 0; k < cnt; ++k) {
+      if (t + k >= Gw) break;                       // uniform across the wave
+      float fl[CPL], fh[CPL];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        fl[2 * i] = bf16_lo(lo[k][i]); fl[2 * i + 1] = bf16_hi(lo[k][i]);
+        fh[2 * i] = bf16_lo(hi[k][i]); fh[2 * i + 1] = bf16_hi(hi[k][i]);
+      }
+      const float s = row16_sum(record_part<CPL>(fl, fh, Qh, Ah));
+      const int j = 16 * (t + k) + 4 * w + quad;
+      if (n == 0 && j < nb) keys[j] = score_key(s);
+    }
+  };
+
+  // ---- interleaved steps: one block + SG record groups each ----
+  const int s0 = a.slot_begin(sh), s1 = a.slot_end(sh);
+  const int nv_l = a.slot_tokens(sh, p2l, unit, L, s0, s1);
+  uint64_t todo = ballot(nv_l > 0);
+  auto pop = [&]() -> int {
+    if (!todo) return -1;
+    const int sl = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    return sl;
+  };
+  bf16x8 ka[AW::KS], kb[AW::KS];
+  i16x4 va[AW::NT], vb[AW::NT];
+  Row la[SG], ha[SG], lb[SG], hb[SG];
+  int steps = 0;
+  int sa = pop();
+  if (sa >= 0) {
+    a.load(s0 + sa, ka, va);
+    load_groups(0, SG, la, ha);
+  }
+  while (sa >= 0) {
+    const int sb = pop();
+    if (sb >= 0) {
+      a.load(s0 + sb, kb, vb);
+      load_groups(SG * (steps + 1), SG, lb, hb);
+    }
+    a.process(ka, va, __builtin_amdgcn_readlane(nv_l, sa), scale_log2);
+    score_groups(SG * steps, SG, la, ha);
+    ++steps;
+    if (sb < 0) break;
+    sa = pop();
+    if (sa >= 0) {
+      a.load(s0 + sa, ka, va);
+      load_groups(SG * (steps + 1), SG, la, ha);
+    }
+    a.process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb), scale_log2);
+    score_groups(SG * steps, SG, lb, hb);
+    ++steps;
+  }
+  // ---- record groups left over: UL at a time ----
+  for (int t = SG * steps; t < Gw; t += UL) {
+    Row lo[UL], hi[UL];
+    load_groups(t, UL, lo, hi);
+    score_groups(t, UL, lo, hi);
+  }
+  a.merge_store(sh, b, h, out, lds);
+}
+
+}  // namespace oasis
