@@ -167,23 +167,54 @@ __global__ __launch_bounds__(kThreads) void evict_kernel(Shape sh, const int32_t
 }
 
 // ------------------------------------------------------------------ prefetch
-// One workgroup per (unit, admission): copies one whole record with 16-byte
-// loads; the source may be host-mapped pinned memory (read over the host link).
-__global__ __launch_bounds__(kThreads) void prefetch_gather_kernel(int K, int NBmax, int rec_bytes,
+// A fixed grid of kGatherGroups workgroups strides over the (unit, admission)
+// items, two records per iteration (16-byte loads, all issued before the
+// stores).  The host link, not the CUs, bounds this copy; a small grid keeps
+// it from taking CU slots from the fused step running on the main stream.
+// The source may be host-mapped pinned memory (read over the host link).
+constexpr int kGatherGroups = 128;
+
+__global__ __launch_bounds__(kThreads) void prefetch_gather_kernel(int units, int K, int NBmax,
+                                                                   int rec_bytes, int max_admit,
                                                                    const uint8_t* __restrict__ rec,
                                                                    uint8_t* __restrict__ pool,
                                                                    const int32_t* __restrict__ admit,
                                                                    const int32_t* __restrict__ admit_count) {
-  const int unit = blockIdx.x;
-  const int k = blockIdx.y;
-  if (k >= admit_count[unit]) return;
-  const int32_t* a = admit + ((size_t)unit * K + k) * 3;
-  const int j = a[0], s = a[1];
-  if (j < 0 || j >= NBmax || s < 0 || s >= K) return;
-  const uint8_t* src = rec + ((size_t)unit * NBmax + j) * rec_bytes;
-  uint8_t* dst = pool + ((size_t)unit * K + s) * rec_bytes;
-  for (int off = threadIdx.x * 16; off < rec_bytes; off += kThreads * 16)
-    *reinterpret_cast<u32x4*>(dst + off) = *reinterpret_cast<const u32x4*>(src + off);
+  const int items = units * max_admit;
+  for (int base = blockIdx.x * 2; base < items; base += gridDim.x * 2) {
+    const uint8_t* src[2];
+    uint8_t* dst[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      src[e] = nullptr;
+      dst[e] = nullptr;
+      const int item = base + e;
+      if (item >= items) continue;
+      const int unit = item / max_admit, k = item % max_admit;
+      if (k >= admit_count[unit]) continue;
+      const int32_t* a = admit + ((size_t)unit * K + k) * 3;
+      const int j = a[0], s = a[1];
+      if (j < 0 || j >= NBmax || s < 0 || s >= K) continue;
+      src[e] = rec + ((size_t)unit * NBmax + j) * rec_bytes;
+      dst[e] = pool + ((size_t)unit * K + s) * rec_bytes;
+    }
+    for (int off = threadIdx.x * 16; off < rec_bytes; off += kThreads * 32) {
+      const int off2 = off + kThreads * 16;
+      u32x4 v[2][2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (!src[e]) continue;
+        v[e][0] = *reinterpret_cast<const u32x4*>(src[e] + off);
+        if (off2 < rec_bytes) v[e][1] = *reinterpret_cast<const u32x4*>(src[e] + off2);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (!dst[e]) continue;
+        *reinterpret_cast<u32x4*>(dst[e] + off) = v[e][0];
+        if (off2 < rec_bytes) *reinterpret_cast<u32x4*>(dst[e] + off2) = v[e][1];
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ fused layer step
@@ -403,9 +434,11 @@ hipError_t launch_prefetch_gather(const Shape& sh, size_t rec_bytes, const void*
                                   const int32_t* admit, const int32_t* admit_count, int max_admit,
                                   hipStream_t st) {
   if (max_admit <= 0) return hipSuccess;
-  dim3 grid(sh.B * sh.H, max_admit);
-  hipLaunchKernelGGL(prefetch_gather_kernel, grid, dim3(kThreads), 0, st, sh.K, sh.NBmax,
-                     (int)rec_bytes, (const uint8_t*)records, (uint8_t*)pool, admit, admit_count);
+  const long long items = (long long)sh.B * sh.H * max_admit;
+  const int groups = (int)(items < 2 * kGatherGroups ? (items + 1) / 2 : kGatherGroups);
+  hipLaunchKernelGGL(prefetch_gather_kernel, dim3(groups), dim3(kThreads), 0, st, sh.B * sh.H, sh.K,
+                     sh.NBmax, (int)rec_bytes, max_admit, (const uint8_t*)records, (uint8_t*)pool,
+                     admit, admit_count);
   return hipGetLastError();
 }
 

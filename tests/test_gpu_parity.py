@@ -449,3 +449,62 @@ def test_full_size_gqa16():
 
 def test_full_size_agentic():
     full_size_check(AGENTIC, 8, 3)
+
+
+# --------------------------------------------------------------------------- edge cases
+EDGE_CASES = [
+    dict(k_resident=1, ctx=1000, batch=2),                       # one slot per unit
+    dict(n_q_heads=2, n_kv_heads=2, k_resident=8),                # G = 1 (2 stacked rows)
+    dict(k_resident=256, ctx=16 * 256 * 2, batch=2),              # largest K
+    dict(k_resident=64, ctx=500, batch=3),                        # fewer blocks than slots
+    dict(dtype="f32", k_resident=5, ctx=333, n_q_heads=3, n_kv_heads=1),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=case_id)
+def test_fused_step_edge_cases(case):
+    cfg = small(**case)
+    ctx = np.array([cfg.ctx, 1, 0][:cfg.batch] if cfg.batch >= 2 else [cfg.ctx], np.int32)
+    if cfg.batch > 3:
+        ctx = np.full(cfg.batch, cfg.ctx, np.int32)
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=13, integer=True)
+    state = gen.random_state(cfg, ctx, nbmax, 13, fill=0.7, stamp_max=2)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    layer.set_state(*state)
+    layer.pool.copy_(pool_from_records(rec, layer.p2l))
+    m = max(1, cfg.max_admit())
+    layer.step(q, 3, m)
+    ref = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, state, 3, m)
+    check_attention(layer.out, ref["out"], cfg.dtype, str(case))
+    np.testing.assert_array_equal(i32(layer.topk_idx), ref["idx"])
+    np.testing.assert_array_equal(i32(layer.p2l), ref["p2l"])
+    np.testing.assert_array_equal(i32(layer.l2p), ref["l2p"])
+    np.testing.assert_array_equal(i32(layer.admit), ref["admit"])
+
+
+def test_empty_resident_set_gives_zero_output():
+    cfg = small(batch=2)
+    ctx, nbmax, rec, q = setup(cfg, [1000, 40], seed=14)
+    layer = Layer(cfg, ctx, nbmax)          # every slot empty
+    layer.summarize(rec)
+    layer.out.fill_(5)
+    lib.lookahead_attn(layer.shape, q, layer.pool, layer.p2l, layer.ctx_len, layer.out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(layer.out).item() == 0
+    # and the fused step fills the empty slots from the top-K, stamping them
+    layer.step(q, 1, cfg.k_resident)
+    torch.cuda.synchronize()
+    assert int(layer.admit_count.sum()) == int(sum(min(cfg.k_resident, -(-c // 16)) for c in ctx)) * cfg.n_kv_heads
+
+
+def test_zero_batch_launches_nothing():
+    cfg = small(batch=1)
+    ctx, nbmax, rec, q = setup(cfg, [300], seed=15)
+    layer = Layer(cfg, ctx, nbmax)
+    empty = lib.Shape.of(cfg, nbmax, batch=0)
+    p = torch.empty(0, device="cuda")
+    raw = lib.raw()
+    import ctypes
+    assert raw.oasis_layer_step(ctypes.byref(empty), *([None] * 4), 0.0, 1, 6, *([None] * 8), None,
+                                0, None) == lib.OK
