@@ -29,26 +29,31 @@ namespace oasis {
 // LDS bytes the bf16 attention merge needs (two [D][17] partial-output
 // buffers, per-wave row max and sum, per-row denominators).
 __host__ __device__ constexpr int attn_lds_bytes(int D, int RT) {
-  return (2 * D * 17 + kWaves * 16 * 2 + 16 * RT) * 4;
+  return (RT * 2 * D * 17 + kWaves * 16 * RT * 2 + 16 * RT) * 4;
 }
 
 // RT = 16-row tiles of the stacked rows (1: up to 16 rows, 2: up to 32).
-// RT == 1: the four waves split the unit's slots four ways.
-// RT == 2: wave w takes row tile w & 1 and slot half w >> 1, so every wave
-// keeps one tile's accumulators; the two waves of a slot half read the same
-// records back to back (the second read is a cache hit), so those loads keep
-// the default cache policy instead of the streaming one.
-template <int D, int RT>
+// By default every wave holds all RT tiles and the four waves split the
+// unit's slots four ways, so each record is fetched once per workgroup.
+// With TW = 1 < RT = 2, wave w takes row tile w & 1 and slot half w >> 1
+// instead (half the accumulators per wave); the two waves of a slot half then
+// read the same records back to back (the second read is a cache hit), so
+// those loads keep the default cache policy instead of the streaming one.
+// TW = row tiles one wave holds.  TW == RT == 2: every wave takes both tiles
+// of its quarter of the slots (each record fetched once per workgroup, twice
+// the accumulators per wave).
+template <int D, int RT, int TW = 1>
 struct AttnWave {
   static constexpr int KS = D / 32;   // logit MFMA steps
   static constexpr int NT = D / 16;   // output tiles
   static constexpr int REC = 2 * kBlock * D;
-  static constexpr int NSPLIT = RT == 2 ? 2 : kWaves;
+  static constexpr bool kPairs = RT == 2 && TW == 1;   // waves paired on a slot half
+  static constexpr int NSPLIT = kPairs ? 2 : kWaves;
 
   int w, g, n, rt, split;
-  bf16x8 qop[KS];
-  float m_run, l_run;
-  f32x4 acc[NT];
+  bf16x8 qop[TW][KS];
+  float m_run[TW], l_run[TW];
+  f32x4 acc[TW][NT];
   const uint16_t* unit_pool;
 
   __device__ __forceinline__ void init(const Shape& sh, const uint16_t* __restrict__ q,
@@ -57,28 +62,31 @@ struct AttnWave {
     w = threadIdx.x / kWave;
     g = lane >> 4;
     n = lane & 15;
-    rt = RT == 2 ? (w & 1) : 0;
-    split = RT == 2 ? (w >> 1) : w;
+    rt = kPairs ? (w & 1) : 0;
+    split = kPairs ? (w >> 1) : w;
     const int G = sh.G;
-    // query operand: lane (g, n) holds row 16*rt + n, channels 32*kk + 8g .. +8
-    const int r = 16 * rt + n;
-    const bool valid = r < 2 * G;
-    const int row = r < G ? 0 : 1;
-    const int head = h * G + (r < G ? r : r - G);
-    const uint16_t* qr = q + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      if (valid) {
-        qop[kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
-      } else {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qop[kk] = __builtin_bit_cast(bf16x8, z);
+    for (int t = 0; t < TW; ++t) {
+      // query operand: lane (g, n) holds row 16*(rt+t) + n, channels 32*kk + 8g .. +8
+      const int r = 16 * (rt + t) + n;
+      const bool valid = r < 2 * G;
+      const int row = r < G ? 0 : 1;
+      const int head = h * G + (r < G ? r : r - G);
+      const uint16_t* qr = q + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (valid) {
+          qop[t][kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
+        } else {
+          u32x4 z = {0u, 0u, 0u, 0u};
+          qop[t][kk] = __builtin_bit_cast(bf16x8, z);
+        }
       }
-    }
-    m_run = -INFINITY;
-    l_run = 0.f;
+      m_run[t] = -INFINITY;
+      l_run[t] = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     unit_pool = pool + (size_t)(b * sh.H + h) * sh.K * REC;
   }
 
@@ -106,106 +114,116 @@ struct AttnWave {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const bf16x8* pk = reinterpret_cast<const bf16x8*>(rec + n * D + 32 * kk + 8 * g);
-      kr[kk] = RT == 1 ? __builtin_nontemporal_load(pk) : *pk;
+      kr[kk] = kPairs ? *pk : __builtin_nontemporal_load(pk);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const i16x4* pv = reinterpret_cast<const i16x4*>(rec + kBlock * D + (16 * nt + n) * kBlock + 4 * g);
-      vr[nt] = RT == 1 ? __builtin_nontemporal_load(pv) : *pv;
+      vr[nt] = kPairs ? *pv : __builtin_nontemporal_load(pv);
     }
   }
 
   __device__ __forceinline__ void process(const bf16x8* kr, const i16x4* vr, int nv, float scale_log2) {
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qop[kk], z, 0, 0, 0);
-    float zz[4];
-    float bm = -INFINITY;
+    for (int t = 0; t < TW; ++t) {
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      zz[i] = (4 * g + i < nv) ? z[i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, zz[i]);
+      for (int kk = 0; kk < KS; ++kk)
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qop[t][kk], z, 0, 0, 0);
+      float zz[4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zz[i] = (4 * g + i < nv) ? z[i] * scale_log2 : -INFINITY;
+        bm = fmaxf(bm, zz[i]);
+      }
+      bm = xrow_max(bm);
+      // f is 1 unless the block max exceeds the running max by more than 8;
+      // multiplying unconditionally keeps the accumulators in place.
+      const bool need = bm > m_run[t] + 8.0f;
+      const float f = need ? exp2f(m_run[t] - bm) : 1.0f;
+      m_run[t] = need ? bm : m_run[t];
+      l_run[t] *= f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[t][nt] *= f;
+      i16x4 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t hb = f32_to_bf16_bits(exp2f(zz[i] - m_run[t]));
+        pb[i] = (short)hb;
+        l_run[t] += bf16_bits_to_f32(hb);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt], pb, acc[t][nt], 0, 0, 0);
     }
-    bm = xrow_max(bm);
-    // f is 1 unless the block max exceeds the running max by more than 8;
-    // multiplying unconditionally keeps the accumulators in place.
-    const bool need = bm > m_run + 8.0f;
-    const float f = need ? exp2f(m_run - bm) : 1.0f;
-    m_run = need ? bm : m_run;
-    l_run *= f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] *= f;
-    i16x4 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t hb = f32_to_bf16_bits(exp2f(zz[i] - m_run));
-      pb[i] = (short)hb;
-      l_run += bf16_bits_to_f32(hb);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt], pb, acc[nt], 0, 0, 0);
   }
 
   // Merges the waves that share a row tile through LDS and writes the rows.
+  // LDS: [2*TW][D][17] partial outputs, [kWaves][16*TW] max and sum, [16*RT].
   __device__ __forceinline__ void merge_store(const Shape& sh, int b, int h,
                                               uint16_t* __restrict__ out, float* lds) const {
     const int tid = threadIdx.x;
     const int G = sh.G;
-    float* obuf = lds;                                   // [2][D][17]
-    float* mbuf = lds + 2 * D * 17;                      // [kWaves][16]
-    float* lbuf = mbuf + kWaves * 16;                    // [kWaves][16]
-    float* lstar = lbuf + kWaves * 16;                   // [16*RT]
-    {
-      const float lsum = xrow_sum(l_run);
+    float* obuf = lds;                                   // [TW][2][D][17]
+    float* mbuf = lds + TW * 2 * D * 17;                 // [kWaves][16*TW]
+    float* lbuf = mbuf + kWaves * 16 * TW;               // [kWaves][16*TW]
+    float* lstar = lbuf + kWaves * 16 * TW;              // [16*RT]
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const float lsum = xrow_sum(l_run[t]);
       if (g == 0) {
-        mbuf[w * 16 + n] = m_run;
-        lbuf[w * 16 + n] = lsum;
+        mbuf[(w * TW + t) * 16 + n] = m_run[t];
+        lbuf[(w * TW + t) * 16 + n] = lsum;
       }
     }
     __syncthreads();
-    float fw = 0.f;
-    {
+    float fw[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
       float M = -INFINITY;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v)
-        if (RT == 1 || (v & 1) == rt) M = fmaxf(M, mbuf[v * 16 + n]);
+        if (!kPairs || (v & 1) == rt) M = fmaxf(M, mbuf[(v * TW + t) * 16 + n]);
       float Ls = 0.f;
+      fw[t] = 0.f;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
-        if (RT == 2 && (v & 1) != rt) continue;
-        const float mv = mbuf[v * 16 + n];
+        if (kPairs && (v & 1) != rt) continue;
+        const float mv = mbuf[(v * TW + t) * 16 + n];
         const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
-        Ls += lbuf[v * 16 + n] * f;
-        if (v == w) fw = f;
+        Ls += lbuf[(v * TW + t) * 16 + n] * f;
+        if (v == w) fw[t] = f;
       }
-      if (w == rt && g == 0) lstar[16 * rt + n] = Ls;
+      if ((kPairs ? w == rt : w == 0) && g == 0) lstar[16 * (rt + t) + n] = Ls;
     }
-    // waves 0,1 write their scaled partial outputs into buffers 0,1; waves 2,3
-    // add theirs (RT == 1: both buffers hold rows 0..15; RT == 2: buffer t
-    // holds row tile t)
+    // waves 0,1 write their scaled partial outputs into buffer pair slot w&1;
+    // waves 2,3 add theirs.  Paired waves: buffer slot = row tile.
     for (int phase = 0; phase < 2; ++phase) {
       if ((w >> 1) == phase) {
-        float* ob = obuf + (w & 1) * D * 17;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int t = 0; t < TW; ++t) {
+          float* ob = obuf + (t * 2 + (w & 1)) * D * 17;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = 16 * nt + 4 * g + i;
-            float* p = ob + c * 17 + n;
-            const float v = acc[nt][i] * fw;
-            if (phase == 0) *p = v; else *p += v;
-          }
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = 16 * nt + 4 * g + i;
+              float* p = ob + c * 17 + n;
+              const float v = acc[t][nt][i] * fw[t];
+              if (phase == 0) *p = v; else *p += v;
+            }
+        }
       }
       __syncthreads();
     }
     const int rows = 2 * G;
     for (int e = tid; e < rows * D; e += kThreads) {
       const int r = e / D, c = e % D;
-      const int rr = r % 16;
-      const float o = RT == 1 ? obuf[c * 17 + rr] + obuf[D * 17 + c * 17 + rr]
-                              : obuf[(r / 16) * D * 17 + c * 17 + rr];
+      const int rr = r % 16, tile = r / 16;
+      float o;
+      if (kPairs) o = obuf[tile * D * 17 + c * 17 + rr];
+      else o = obuf[(tile * 2) * D * 17 + c * 17 + rr] + obuf[(tile * 2 + 1) * D * 17 + c * 17 + rr];
       const float Ls = lstar[r];
       const int row = r < G ? 0 : 1;
       const int head = h * G + (r < G ? r : r - G);
@@ -214,13 +232,13 @@ struct AttnWave {
   }
 };
 
-template <int D, int RT>
+template <int D, int RT, int TW = RT>
 __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
                                                const uint16_t* __restrict__ pool,
                                                const int32_t* __restrict__ p2l, int b, int h,
                                                int L, float scale_log2,
                                                uint16_t* __restrict__ out, float* lds) {
-  using AW = AttnWave<D, RT>;
+  using AW = AttnWave<D, RT, TW>;
   AW a;
   a.init(sh, q, pool, b, h);
   const int unit = b * sh.H + h;

@@ -20,7 +20,7 @@ namespace oasis {
 // row tile, K <= 128 with two).  Writes keys[j] for j < nb and the attention
 // output; ends with the attention merge (so the keys are complete in LDS for
 // the whole workgroup afterwards).
-template <int D, int RT, int SG, int UL>
+template <int D, int RT, int SG, int UL, int TW = RT>
 __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ pool,
                                                     const int32_t* __restrict__ p2l,
@@ -28,7 +28,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
                                                     int b, int h, int L, float scale_log2,
                                                     uint16_t* __restrict__ out, float* lds,
                                                     uint32_t* keys) {
-  using AW = AttnWave<D, RT>;
+  using AW = AttnWave<D, RT, TW>;
   constexpr int CPL = D / 16;
   constexpr int RW = CPL / 2;          // 32-bit words of one summary row slice
   AW a;
