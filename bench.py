@@ -95,6 +95,32 @@ def cpu_baseline(cfg, ctx, records_host, qs_host, min_cpu_seconds: float):
                       f"eviction) in {spent:.2f} s wall on {nth} threads"}
 
 
+def dense_leg(cfg, layer, rec_host, q, reps: int = 10):
+    """The dense comparator on the same layer: attention of both rows over the
+    full KV held in HBM (the capacity the method avoids needing)."""
+    import torch
+    from sparse_kv_block_amd import lib
+    rec = rec_host.to("cuda")
+    ws = lib.dense_attn_workspace(layer.shape)
+    out = torch.empty_like(layer.out)
+    for _ in range(2):
+        lib.dense_attn(layer.shape, q, rec, layer.ctx_len, out, ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        lib.dense_attn(layer.shape, q, rec, layer.ctx_len, out, ws)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    kv = rec.numel() * rec.element_size()
+    del rec, ws
+    torch.cuda.empty_cache()
+    log(f"[bench] dense attention over {kv / 2**30:.1f} GiB of KV: {us:.1f} us, {kv / us / 1e3:.0f} GB/s")
+    return {"us": round(us, 2), "kv_bytes": kv, "GBps": round(kv / us / 1e3, 1),
+            "hbm_kv_per_layer_GiB": round(kv / 2**30, 2)}
+
+
 def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
     """The 36-layer decode step with the fetch-cap sweep: per layer the fused
     step on the main stream and the gather prefetch of its admissions on a side
@@ -183,6 +209,8 @@ def main():
     ap.add_argument("--pipeline", action="store_true",
                     help="also run the 36-layer decode step with the fetch-cap sweep")
     ap.add_argument("--pipeline-steps", type=int, default=3)
+    ap.add_argument("--dense", action="store_true",
+                    help="also time the dense comparator (attention over the full HBM-resident KV)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, launch a plain elementwise copy of this many MiB "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -225,6 +253,9 @@ def main():
     layer.cold_fill(qs[0], rec_host)
     torch.cuda.synchronize()
     log("[bench] cold fill done")
+    dense = None
+    if args.dense:
+        dense = dense_leg(cfg, layer, rec_host, qs[0])
 
     stream = torch.cuda.current_stream()
     step = 0
@@ -310,6 +341,9 @@ def main():
         log(f"[bench] prefetch {nbytes / 1e6:.1f} MB: gather {res['gather']['GBps']} GB/s, "
             f"memcpy {res['memcpy']['GBps']} GB/s")
 
+    if dense is not None:
+        dense["sparse_step_speedup"] = round(dense["us"] / (avg_kernel_s * 1e6), 2)
+        result["dense_comparator"] = dense
     if args.pipeline:
         result["pipeline_36_layer"] = pipeline_leg(layer, rec_host, args.pipeline_steps, 2)
 

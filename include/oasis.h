@@ -218,6 +218,19 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Dense comparator (not part of the look-ahead method) — decode attention of
+ * both rows of every query head over every valid token of the full KV,
+ * `records` [B][Hkv][NBmax][record] in device memory: the dense baseline the
+ * pages compare against (agihunt.info summary, throughput table: dense vLLM).
+ * Same output convention as oasis_lookahead_attn.  bf16 only.  `workspace`
+ * (device memory, at least oasis_dense_attn_workspace_bytes(shape) bytes)
+ * holds per-128-block partial results. */
+size_t oasis_dense_attn_workspace_bytes(const oasis_shape* shape);
+oasis_status oasis_dense_attn(const oasis_shape* shape, const void* q,
+                              const void* records, const int32_t* ctx_len,
+                              float scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,7 +86,7 @@ size_t esize(const oasis_shape* s) { return s->dtype == OASIS_DTYPE_F32 ? 4 : 2;
 
 extern "C" {
 
-int32_t oasis_abi_version(void) { return 2; }
+int32_t oasis_abi_version(void) { return 3; }
 
 const char* oasis_last_error(void) { return g_error.c_str(); }
 
@@ -297,6 +297,33 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const voi
                                              scale, step, max_admit, out, topk_idx, topk_score, l2p,
                                              p2l, last_sel, admit, admit_count,
                                              need > 0 ? workspace : nullptr, (hipStream_t)stream),
+                    fn);
+}
+
+size_t oasis_dense_attn_workspace_bytes(const oasis_shape* shape) {
+  if (check_shape(shape, "oasis_dense_attn_workspace_bytes") != OASIS_OK) return 0;
+  return oasis::dense_workspace_bytes(to_shape(shape));
+}
+
+oasis_status oasis_dense_attn(const oasis_shape* shape, const void* q, const void* records,
+                              const int32_t* ctx_len, float scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const char* fn = "oasis_dense_attn";
+  if (oasis_status st = check_shape(shape, fn)) return st;
+  if (shape->dtype != OASIS_DTYPE_BF16)
+    return fail(OASIS_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (isnan(scale) || isinf(scale)) return fail(OASIS_ERR_INVALID, "%s: scale is not finite", fn);
+  if (shape->batch == 0) return OASIS_OK;
+  OASIS_NONNULL(q, fn);
+  OASIS_NONNULL(records, fn);
+  OASIS_NONNULL(ctx_len, fn);
+  OASIS_NONNULL(out, fn);
+  OASIS_NONNULL(workspace, fn);
+  const size_t need = oasis::dense_workspace_bytes(to_shape(shape));
+  if (workspace_bytes < need)
+    return fail(OASIS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  return hip_status(oasis::launch_dense_attn(to_shape(shape), q, records, ctx_len, scale, out,
+                                             workspace, (hipStream_t)stream),
                     fn);
 }
 

@@ -29,7 +29,7 @@ namespace oasis {
 // LDS bytes the bf16 attention merge needs (two [D][17] partial-output
 // buffers, per-wave row max and sum, per-row denominators).
 __host__ __device__ constexpr int attn_lds_bytes(int D, int RT) {
-  return (RT * 2 * D * 17 + kWaves * 16 * RT * 2 + 16 * RT) * 4;
+  return (RT * 2 * D * 17 + kWaves * 16 * RT * 2 + 2 * 16 * RT) * 4;
 }
 
 // RT = 16-row tiles of the stacked rows (1: up to 16 rows, 2: up to 32).
@@ -56,8 +56,10 @@ struct AttnWave {
   f32x4 acc[TW][NT];
   const uint16_t* unit_pool;
 
+  // unit_base: the unit's first record (slot 0 of its pool, or block 0 of its
+  // records for the dense variant).
   __device__ __forceinline__ void init(const Shape& sh, const uint16_t* __restrict__ q,
-                                       const uint16_t* __restrict__ pool, int b, int h) {
+                                       const uint16_t* __restrict__ unit_base, int b, int h) {
     const int lane = threadIdx.x % kWave;
     w = threadIdx.x / kWave;
     g = lane >> 4;
@@ -87,7 +89,7 @@ struct AttnWave {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    unit_pool = pool + (size_t)(b * sh.H + h) * sh.K * REC;
+    unit_pool = unit_base;
   }
 
   // This wave's slot range.
@@ -159,16 +161,20 @@ struct AttnWave {
     }
   }
 
-  // Merges the waves that share a row tile through LDS and writes the rows.
-  // LDS: [2*TW][D][17] partial outputs, [kWaves][16*TW] max and sum, [16*RT].
+  // Merges the waves that share a row tile through LDS and writes the rows:
+  // normalised bf16 rows to `out`, or, when `part` is given, the unnormalised
+  // partial (running max, sum, output row) of each row to part[r][0 .. D+2).
+  // LDS: [2*TW][D][17] partial outputs, [kWaves][16*TW] max and sum, [16*RT] x 2.
   __device__ __forceinline__ void merge_store(const Shape& sh, int b, int h,
-                                              uint16_t* __restrict__ out, float* lds) const {
+                                              uint16_t* __restrict__ out, float* lds,
+                                              float* __restrict__ part = nullptr) const {
     const int tid = threadIdx.x;
     const int G = sh.G;
     float* obuf = lds;                                   // [TW][2][D][17]
     float* mbuf = lds + TW * 2 * D * 17;                 // [kWaves][16*TW]
     float* lbuf = mbuf + kWaves * 16 * TW;               // [kWaves][16*TW]
     float* lstar = lbuf + kWaves * 16 * TW;              // [16*RT]
+    float* mstar = lstar + 16 * RT;                      // [16*RT]
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
       const float lsum = xrow_sum(l_run[t]);
@@ -195,7 +201,10 @@ struct AttnWave {
         Ls += lbuf[(v * TW + t) * 16 + n] * f;
         if (v == w) fw[t] = f;
       }
-      if ((kPairs ? w == rt : w == 0) && g == 0) lstar[16 * (rt + t) + n] = Ls;
+      if ((kPairs ? w == rt : w == 0) && g == 0) {
+        lstar[16 * (rt + t) + n] = Ls;
+        mstar[16 * (rt + t) + n] = M;
+      }
     }
     // waves 0,1 write their scaled partial outputs into buffer pair slot w&1;
     // waves 2,3 add theirs.  Paired waves: buffer slot = row tile.
@@ -225,6 +234,12 @@ struct AttnWave {
       if (kPairs) o = obuf[tile * D * 17 + c * 17 + rr];
       else o = obuf[(tile * 2) * D * 17 + c * 17 + rr] + obuf[(tile * 2 + 1) * D * 17 + c * 17 + rr];
       const float Ls = lstar[r];
+      if (part) {
+        float* pr = part + (size_t)r * (D + 2);
+        if (c == 0) { pr[0] = mstar[r]; pr[1] = Ls; }
+        pr[2 + c] = o;
+        continue;
+      }
       const int row = r < G ? 0 : 1;
       const int head = h * G + (r < G ? r : r - G);
       out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(Ls > 0.f ? o / Ls : 0.f);
@@ -240,8 +255,8 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
                                                uint16_t* __restrict__ out, float* lds) {
   using AW = AttnWave<D, RT, TW>;
   AW a;
-  a.init(sh, q, pool, b, h);
   const int unit = b * sh.H + h;
+  a.init(sh, q, pool + (size_t)unit * sh.K * AW::REC, b, h);
   // This wave's slots, 64 at a time; within a group two register buffers
   // alternate: while one block is processed the next one's loads are in flight.
   const int s0 = a.slot_begin(sh), s1 = a.slot_end(sh);

@@ -349,6 +349,95 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
              admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
 }
 
+// ------------------------------------------------------------------ dense attention
+// The dense comparator: decode attention of both rows over every valid token
+// of the full, HBM-resident KV.  Split over the context: workgroup (unit, c)
+// runs the same per-wave MFMA core over blocks [c*128, (c+1)*128) and writes
+// the unnormalised partial (max, sum, output row) of every row; a second
+// kernel merges the partials of a unit.
+constexpr int kDenseChunk = 4 * kWave / 2;   // 128 blocks: 32 per wave
+
+template <int D, int RT>
+__global__ __launch_bounds__(kThreads) void dense_partial_kernel(Shape sh, const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ rec,
+                                                                 const int32_t* __restrict__ ctx,
+                                                                 float scale_log2, int chunks,
+                                                                 float* __restrict__ part) {
+  extern __shared__ __align__(16) char smem[];
+  using AW = AttnWave<D, RT, RT>;
+  const int units = sh.B * sh.H;
+  const int unit = blockIdx.x % units, c = blockIdx.x / units;
+  const int b = unit / sh.H, h = unit % sh.H;
+  const int L = ctx[b];
+  const int nb = n_blocks(L, sh.NBmax);
+  const int rows = 2 * sh.G;
+  float* mypart = part + ((size_t)unit * chunks + c) * rows * (D + 2);
+  const int j0 = c * kDenseChunk;
+  if (j0 >= nb) {                                   // nothing in this chunk
+    for (int r = threadIdx.x; r < rows; r += kThreads) {
+      mypart[(size_t)r * (D + 2)] = -INFINITY;
+      mypart[(size_t)r * (D + 2) + 1] = 0.f;
+    }
+    return;
+  }
+  AW a;
+  a.init(sh, q, rec + (size_t)unit * sh.NBmax * AW::REC, b, h);
+  const int lane = threadIdx.x % kWave;
+  const int jw = j0 + a.w * (kDenseChunk / kWaves);
+  int nv_l = 0;
+  if (lane < kDenseChunk / kWaves && jw + lane < nb) {
+    const int nv = L - (jw + lane) * kBlock;
+    nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
+  }
+  uint64_t todo = ballot(nv_l > 0);
+  auto pop = [&]() -> int {
+    if (!todo) return -1;
+    const int sl = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    return sl;
+  };
+  bf16x8 ka[AW::KS], kb[AW::KS];
+  i16x4 va[AW::NT], vb[AW::NT];
+  int sa = pop();
+  if (sa >= 0) a.load(jw + sa, ka, va);
+  while (sa >= 0) {
+    const int sb = pop();
+    if (sb >= 0) a.load(jw + sb, kb, vb);
+    a.process(ka, va, __builtin_amdgcn_readlane(nv_l, sa), scale_log2);
+    if (sb < 0) break;
+    sa = pop();
+    if (sa >= 0) a.load(jw + sa, ka, va);
+    a.process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb), scale_log2);
+  }
+  a.merge_store(sh, b, h, nullptr, reinterpret_cast<float*>(smem), mypart);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void dense_merge_kernel(Shape sh, int chunks,
+                                                               const float* __restrict__ part,
+                                                               uint16_t* __restrict__ out) {
+  const int unit = blockIdx.x;
+  const int b = unit / sh.H, h = unit % sh.H;
+  const int G = sh.G, rows = 2 * G;
+  const float* up = part + (size_t)unit * chunks * rows * (D + 2);
+  for (int e = threadIdx.x; e < rows * D; e += kThreads) {
+    const int r = e / D, c = e % D;
+    float M = -INFINITY;
+    for (int k = 0; k < chunks; ++k) M = fmaxf(M, up[((size_t)k * rows + r) * (D + 2)]);
+    float Ls = 0.f, o = 0.f;
+    for (int k = 0; k < chunks; ++k) {
+      const float* pr = up + ((size_t)k * rows + r) * (D + 2);
+      if (pr[0] == -INFINITY) continue;
+      const float f = exp2f(pr[0] - M);
+      Ls += pr[1] * f;
+      o += pr[2 + c] * f;
+    }
+    const int row = r < G ? 0 : 1;
+    const int head = h * G + (r < G ? r : r - G);
+    out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(Ls > 0.f ? o / Ls : 0.f);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
@@ -488,6 +577,34 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     if (sh.d == 128) OASIS_STEP32(128); else OASIS_STEP32(64);
 #undef OASIS_STEP32
   }
+  return hipGetLastError();
+}
+
+size_t dense_workspace_bytes(const Shape& sh) {
+  const int chunks = (sh.NBmax + kDenseChunk - 1) / kDenseChunk;
+  return (size_t)sh.B * sh.H * chunks * 2 * sh.G * (sh.d + 2) * sizeof(float);
+}
+
+hipError_t launch_dense_attn(const Shape& sh, const void* q, const void* records, const int32_t* ctx,
+                             float scale, void* out, void* workspace, hipStream_t st) {
+  const float sl = scale_or_default(scale, sh.d) * kLog2e;
+  const int chunks = (sh.NBmax + kDenseChunk - 1) / kDenseChunk;
+  const int units = sh.B * sh.H;
+  const int rt = rt_of(sh.G);
+  const size_t lds = attn_lds_bytes(sh.d, rt);
+  float* part = static_cast<float*>(workspace);
+#define OASIS_DENSE(D_, RT_)                                                                    \
+  hipLaunchKernelGGL((dense_partial_kernel<D_, RT_>), dim3(units * chunks), dim3(kThreads), lds, \
+                     st, sh, (const uint16_t*)q, (const uint16_t*)records, ctx, sl, chunks, part)
+  if (sh.d == 128) { if (rt == 1) OASIS_DENSE(128, 1); else OASIS_DENSE(128, 2); }
+  else             { if (rt == 1) OASIS_DENSE(64, 1);  else OASIS_DENSE(64, 2); }
+#undef OASIS_DENSE
+  if (sh.d == 128)
+    hipLaunchKernelGGL(dense_merge_kernel<128>, dim3(units), dim3(kThreads), 0, st, sh, chunks, part,
+                       (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(dense_merge_kernel<64>, dim3(units), dim3(kThreads), 0, st, sh, chunks, part,
+                       (uint16_t*)out);
   return hipGetLastError();
 }
 

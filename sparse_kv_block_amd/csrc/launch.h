@@ -29,4 +29,9 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
                              int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
                              int32_t* admit_count, void* workspace, hipStream_t st);
 
+size_t dense_workspace_bytes(const Shape& sh);
+hipError_t launch_dense_attn(const Shape& sh, const void* q, const void* records,
+                             const int32_t* ctx_len, float scale, void* out, void* workspace,
+                             hipStream_t st);
+
 }  // namespace oasis

@@ -32,8 +32,8 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   constexpr int CPL = D / 16;
   constexpr int RW = CPL / 2;          // 32-bit words of one summary row slice
   AW a;
-  a.init(sh, q, pool, b, h);
   const int unit = b * sh.H + h;
+  a.init(sh, q, pool + (size_t)unit * sh.K * AW::REC, b, h);
   const int w = a.w, quad = a.g, n = a.n;
   const int c0 = n * CPL;
   float Qh[CPL], Ah[CPL];

@@ -28,7 +28,7 @@ SYMBOLS = ("oasis_abi_version", "oasis_last_error", "oasis_cap_to_max_admit",
            "oasis_record_bytes", "oasis_summary_bytes", "oasis_host_to_device_ptr",
            "oasis_summarize", "oasis_lookahead_attn", "oasis_score_topk",
            "oasis_capped_evict", "oasis_prefetch", "oasis_layer_step",
-           "oasis_layer_step_workspace_bytes")
+           "oasis_layer_step_workspace_bytes", "oasis_dense_attn", "oasis_dense_attn_workspace_bytes")
 
 
 class OasisError(RuntimeError):
@@ -81,6 +81,8 @@ def _load():
         "oasis_layer_step": ([SP, P, P, P, P, F, I32, I32, P, P, P, P, P, P, P, P, P,
                               ctypes.c_size_t, P], I32),
         "oasis_layer_step_workspace_bytes": ([SP], ctypes.c_size_t),
+        "oasis_dense_attn": ([SP, P, P, P, F, P, P, ctypes.c_size_t, P], I32),
+        "oasis_dense_attn_workspace_bytes": ([SP], ctypes.c_size_t),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -255,3 +257,23 @@ def layer_step(shape: Shape, q, pool, summ, ctx_len, step: int, max_admit: int, 
         _dev(l2p, "l2p", I32, U * shape.max_blocks), _dev(p2l, "p2l", I32, U * K),
         _dev(last_sel, "last_sel", I32, U * K), _dev(admit, "admit", I32, U * K * 3),
         _dev(admit_count, "admit_count", I32, U), *_workspace(shape, workspace), _stream(stream)))
+
+
+def dense_attn_workspace(shape: Shape, device="cuda"):
+    n = int(_lib.oasis_dense_attn_workspace_bytes(ctypes.byref(shape)))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def dense_attn(shape: Shape, q, records, ctx_len, out, workspace, scale: float = 0.0, stream=None):
+    """Dense comparator: attention over every valid token of `records` (device)."""
+    dt, U, d = shape.torch_dtype(), shape.units(), shape.head_dim
+    qn = shape.batch * 2 * shape.n_q_heads * d
+    need = int(_lib.oasis_dense_attn_workspace_bytes(ctypes.byref(shape)))
+    if workspace.device.type != "cuda" or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"dense attention needs a device workspace of >= {need} bytes")
+    _check(_lib.oasis_dense_attn(
+        ctypes.byref(shape), _dev(q, "q", dt, qn),
+        _dev(records, "records", dt, U * shape.max_blocks * shape.record_elems()),
+        _dev(ctx_len, "ctx_len", I32, shape.batch), float(scale), _dev(out, "out", dt, qn),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
