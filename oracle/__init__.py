@@ -47,8 +47,9 @@ def lib():
                                        P, P, P, P, P, P, I]
         L.ora_attention.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, D, P, P, I, I]
         L.ora_prefetch.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, I]
+        L.ora_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
         for f in (L.ora_summarize, L.ora_block_scores, L.ora_topk, L.ora_capped_evict,
-                  L.ora_attention, L.ora_prefetch):
+                  L.ora_attention, L.ora_prefetch, L.ora_append):
             f.restype = None
         _lib = L
     return _lib
@@ -196,6 +197,19 @@ def prefetch(records, pool, admit, admit_count, block_size: int, units=None):
     lib().ora_prefetch(B, H, NB, block_size, d, K, dtype_code(rec), _ptr(rec), _ptr(pool),
                        _ptr(ad), _ptr(ac), _ptr(u), nu)
     return pool
+
+
+def append(k_new, v_new, records, summ, ctx_len, block_size: int, pool=None, l2p=None):
+    """In place on the numpy arrays records, summ, ctx_len (and pool)."""
+    kn, vn = as_np(k_new), as_np(v_new)
+    for a in (records, summ, ctx_len):
+        assert isinstance(a, np.ndarray) and a.flags.c_contiguous
+    B, H, NB, E = records.shape
+    d = E // (2 * block_size)
+    K = pool.shape[2] if pool is not None else 0
+    l2 = None if l2p is None else np.ascontiguousarray(l2p, dtype=np.int32)
+    lib().ora_append(B, H, NB, block_size, d, K, dtype_code(records), _ptr(kn), _ptr(vn),
+                     _ptr(records), _ptr(pool), _ptr(l2), _ptr(summ), _ptr(ctx_len))
 
 
 def layer_step(q, records, summ, ctx_len, block_size: int, K: int, step: int,

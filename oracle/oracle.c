@@ -394,3 +394,51 @@ void ora_prefetch(int B, int H, int NBmax, int S, int d, int K, int dtype,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode append (the token the next step adds to the context).  The summary
+ * of the tail block is recomputed from its stored keys, which is the plain
+ * definition of the min/max over the block's valid tokens.                  */
+
+void ora_append(int B, int H, int NBmax, int S, int d, int K, int dtype,
+                const void* k_new, const void* v_new, void* records, void* pool,
+                const int32_t* l2p, void* summ, int32_t* ctx_len) {
+    size_t es = esize(dtype);
+    size_t rec_elems = (size_t)2 * S * d;
+    for (int b = 0; b < B; ++b) {
+        int32_t t = ctx_len[b];
+        if (t < 0 || t >= NBmax * S) continue;
+        int j = t / S, u = t % S;
+        for (int h = 0; h < H; ++h) {
+            int unit = b * H + h;
+            char* rec = (char*)records + ((size_t)unit * NBmax + j) * rec_elems * es;
+            for (int c = 0; c < d; ++c) {
+                memcpy(rec + ((size_t)u * d + c) * es,
+                       (const char*)k_new + ((size_t)unit * d + c) * es, es);
+                memcpy(rec + ((size_t)S * d + (size_t)c * S + u) * es,
+                       (const char*)v_new + ((size_t)unit * d + c) * es, es);
+            }
+            if (pool) {
+                int32_t s = l2p[(size_t)unit * NBmax + j];
+                if (s >= 0 && s < K)
+                    memcpy((char*)pool + ((size_t)unit * K + s) * rec_elems * es, rec,
+                           rec_elems * es);
+            }
+            /* summary of block j over its tokens 0..u */
+            size_t sbase = ((size_t)unit * NBmax + j) * 2 * (size_t)d;
+            for (int c = 0; c < d; ++c) {
+                size_t imin = (size_t)c, imax = (size_t)c;
+                double vmin = elem(rec, dtype, imin), vmax = vmin;
+                for (int v = 1; v <= u; ++v) {
+                    size_t i = (size_t)v * d + c;
+                    double x = elem(rec, dtype, i);
+                    if (x < vmin) { vmin = x; imin = i; }
+                    if (x > vmax) { vmax = x; imax = i; }
+                }
+                memcpy((char*)summ + (sbase + c) * es, rec + imin * es, es);
+                memcpy((char*)summ + (sbase + d + c) * es, rec + imax * es, es);
+            }
+        }
+        ctx_len[b] = t + 1;
+    }
+}

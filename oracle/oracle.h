@@ -71,6 +71,16 @@ void ora_prefetch(int B, int H, int NBmax, int S, int d, int K, int dtype,
                   const void* records, void* pool, const int32_t* admit,
                   const int32_t* admit_count, const int32_t* units, int n_units);
 
+/* Decode append: request b's new token (position t = ctx_len[b]) goes into
+ * key row t%S and value column t%S of block t/S of records (and of pool slot
+ * l2p[block] when that block is resident; pool may be NULL); the block's
+ * summary becomes min/max over its tokens 0..t%S; ctx_len[b] grows by one.
+ * Requests whose next position is past NBmax*S are left unchanged.
+ * k_new, v_new: [B][H][d]. */
+void ora_append(int B, int H, int NBmax, int S, int d, int K, int dtype,
+                const void* k_new, const void* v_new, void* records, void* pool,
+                const int32_t* l2p, void* summ, int32_t* ctx_len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -379,3 +379,49 @@ def test_kv_bytes_per_request_is_the_pages_86_gb():
     # bf16 K and V).
     per_token = 64 * 8 * 128 * 2 * 2
     assert abs(per_token * 32.7e3 / 1e9 - 8.6) < 0.05
+
+
+# --------------------------------------------------------------------------
+# Decode append
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_places_tokens_and_keeps_summaries_exact(ora, dtype):
+    # Appending tokens one at a time must give the same records as placing
+    # them directly (key row t%S, value column t%S of block t/S) and summaries
+    # equal to a fresh summarize of the result (itself pinned to numpy).
+    cfg = tiny(dtype=dtype, batch=3, head_dim=8, block_size=4, k_resident=3)
+    ctx0 = np.array([5, 0, 12], np.int32)          # mid-block, empty, block boundary
+    nb = 6                                         # capacity 24 tokens
+    ctx, _, rec, _ = make(cfg, ctx0, nbmax=nb, seed=21)
+    rec = ora.as_np(rec).copy()
+    summ = ora.summarize(rec, ctx0, 4)
+    ctx = ctx0.copy()
+    rng = np.random.default_rng(3)
+    H, d, S = cfg.n_kv_heads, cfg.head_dim, cfg.block_size
+    expect = rec.copy()
+    pool = np.zeros((3, H, 3, rec.shape[-1]), rec.dtype)
+    l2p = np.full((3, H, nb), -1, np.int32)
+    l2p[2, 1, 3] = 2                               # block 3 of request 2, head 1 resident
+    pool[2, 1, 2] = rec[2, 1, 3]
+    for step in range(14):
+        kf = rng.integers(-4, 5, size=(3, H, d)).astype(np.float32)
+        vf = rng.integers(-4, 5, size=(3, H, d)).astype(np.float32)
+        if dtype == "bf16":
+            kn = (kf.view(np.uint32) >> 16).astype(np.uint16)
+            vn = (vf.view(np.uint32) >> 16).astype(np.uint16)
+        else:
+            kn, vn = kf, vf
+        for b in range(3):
+            t = ctx[b]
+            if t >= nb * S:
+                continue
+            j, u = divmod(int(t), S)
+            for h in range(H):
+                expect[b, h, j, u * d:(u + 1) * d] = kn[b, h]
+                expect[b, h, j, S * d + u::S][:d] = vn[b, h]
+        before = ctx.copy()
+        ora.append(kn, vn, rec, summ, ctx, S, pool=pool, l2p=l2p)
+        np.testing.assert_array_equal(ctx, np.where(before >= nb * S, before, before + 1))
+    np.testing.assert_array_equal(rec, expect)
+    np.testing.assert_array_equal(ora.to_f64(summ), ora.to_f64(ora.summarize(rec, ctx, S)))
+    np.testing.assert_array_equal(pool[2, 1, 2], rec[2, 1, 3])
+    assert ctx.tolist() == [19, 14, 24]            # request 2 stopped at capacity
