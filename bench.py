@@ -121,6 +121,32 @@ def dense_leg(cfg, layer, rec_host, q, reps: int = 10):
             "hbm_kv_per_layer_GiB": round(kv / 2**30, 2)}
 
 
+def append_leg(layer, rec_host, reps: int = 8):
+    """Decode append of one token per request into the pinned host records
+    (written over the host link), the resident copies and the summaries."""
+    import torch
+    from sparse_kv_block_amd import gen
+    cfg = layer.cfg
+    kn, vn = gen.new_tokens(cfg, reps + 1, seed=77, device=layer.device)
+    stream = torch.cuda.current_stream()
+    layer.append(rec_host, kn[0], vn[0])                       # warm-up
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        layer.append(rec_host, kn[i + 1], vn[i + 1])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    es = 2 if cfg.dtype == "bf16" else 4
+    units = cfg.batch * cfg.n_kv_heads
+    res = {"us": round(us, 2), "records": "pinned host (host-mapped)",
+           "host_link_bytes": units * 2 * cfg.head_dim * es,
+           "hbm_bytes_summaries": units * 2 * 2 * cfg.head_dim * es}
+    log(f"[bench] append: {us:.1f} us per token step ({units} units)")
+    return res
+
+
 def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
     """The 36-layer decode step with the fetch-cap sweep: per layer the fused
     step on the main stream and the gather prefetch of its admissions on a side
@@ -211,6 +237,8 @@ def main():
     ap.add_argument("--pipeline-steps", type=int, default=3)
     ap.add_argument("--dense", action="store_true",
                     help="also time the dense comparator (attention over the full HBM-resident KV)")
+    ap.add_argument("--append", action="store_true",
+                    help="also time the decode append (after every other GPU leg)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, launch a plain elementwise copy of this many MiB "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -346,6 +374,9 @@ def main():
         result["dense_comparator"] = dense
     if args.pipeline:
         result["pipeline_36_layer"] = pipeline_leg(layer, rec_host, args.pipeline_steps, 2)
+
+    if args.append:
+        result["append"] = append_leg(layer, rec_host)
 
     if not args.no_cpu_baseline:
         log(f"[bench] oracle baseline ...")

@@ -192,6 +192,29 @@ oasis_status oasis_prefetch(const oasis_shape* shape, const void* records,
                             int32_t mode, int32_t* host_staging,
                             void* side_stream, void* wait_before, void* done);
 
+/* Decode append (the step on either side of the layer step in a decode
+ * loop).  The pith.science paper page ("What carries the argument") keeps the
+ * full KV off HBM and the block summaries in HBM; the pages do not spell out
+ * how a new token enters them, so this call takes the plain reading: the
+ * token joins the block record that holds its position, the resident copy of
+ * that block when it is resident, and that block's summary, and the context
+ * grows by one.  For every request b with t = ctx_len[b] in [0, NBmax*16):
+ * for every KV head h, k_new[b][h][:] becomes key row t%16 and v_new[b][h][:]
+ * value column t%16 of records[b][h][t/16]; if pool is given and
+ * l2p[b][h][t/16] = s is in [0, K), the same row and column are written into
+ * pool slot s; summ[b][h][t/16] becomes (k, k) for the block's first token,
+ * else its min/max widen to include k (a tie keeps the stored value); then
+ * ctx_len[b] = t + 1.  Other requests are left unchanged.
+ *   k_new, v_new  [B][Hkv][d] device memory, element type of the shape
+ *   records       full KV, device or host-mapped pinned memory (written)
+ *   pool, l2p     resident slots and slot map (device), both or neither NULL
+ *   summ, ctx_len device memory (written)
+ * Tokens earlier in the block must already be in records and summ. */
+oasis_status oasis_append_token(const oasis_shape* shape, const void* k_new,
+                                const void* v_new, void* records, void* pool,
+                                const int32_t* l2p, void* summ,
+                                int32_t* ctx_len, void* stream);
+
 /* Workspace bytes oasis_layer_step needs for a shape: 0 while
  * max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K lists
  * of the split summary scan and one counter per unit). */

@@ -86,7 +86,7 @@ size_t esize(const oasis_shape* s) { return s->dtype == OASIS_DTYPE_F32 ? 4 : 2;
 
 extern "C" {
 
-int32_t oasis_abi_version(void) { return 3; }
+int32_t oasis_abi_version(void) { return 4; }
 
 const char* oasis_last_error(void) { return g_error.c_str(); }
 
@@ -251,6 +251,24 @@ oasis_status oasis_prefetch(const oasis_shape* shape, const void* records, void*
     if (oasis_status s = hip_status(hipEventRecord((hipEvent_t)done, st), fn)) return s;
   }
   return OASIS_OK;
+}
+
+oasis_status oasis_append_token(const oasis_shape* shape, const void* k_new, const void* v_new,
+                                void* records, void* pool, const int32_t* l2p, void* summ,
+                                int32_t* ctx_len, void* stream) {
+  const char* fn = "oasis_append_token";
+  if (oasis_status st = check_shape(shape, fn)) return st;
+  if (shape->batch == 0) return OASIS_OK;
+  OASIS_NONNULL(k_new, fn);
+  OASIS_NONNULL(v_new, fn);
+  OASIS_NONNULL(records, fn);
+  OASIS_NONNULL(summ, fn);
+  OASIS_NONNULL(ctx_len, fn);
+  if ((pool == nullptr) != (l2p == nullptr))
+    return fail(OASIS_ERR_INVALID, "%s: pool and l2p must both be given or both be NULL", fn);
+  return hip_status(oasis::launch_append(to_shape(shape), shape->dtype, k_new, v_new, records, pool,
+                                         l2p, summ, ctx_len, (hipStream_t)stream),
+                    fn);
 }
 
 size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape) {

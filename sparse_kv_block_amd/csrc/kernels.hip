@@ -217,6 +217,61 @@ __global__ __launch_bounds__(kThreads) void prefetch_gather_kernel(int units, in
   }
 }
 
+// ------------------------------------------------------------------ decode append
+// One workgroup per request: the request's next position t = ctx_len[b] names
+// block j = t / 16 and row u = t % 16.  Thread (h, c) writes channel c of the
+// new key into key row u and of the new value into value column u of record
+// (b, h, j) in the full KV (device or host-mapped), and into the resident
+// copy when the slot map holds block j; the block's summary takes the new key
+// (the first token of a block sets both bounds, later tokens widen them; a
+// tie keeps the stored value).  After a barrier thread 0 grows ctx_len[b], so
+// every thread has read the old length first.
+__device__ __forceinline__ float elem_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+__device__ __forceinline__ float elem_f32(float x) { return x; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void append_kernel(Shape sh, const T* __restrict__ k_new,
+                                                          const T* __restrict__ v_new,
+                                                          T* __restrict__ rec, T* __restrict__ pool,
+                                                          const int32_t* __restrict__ l2p,
+                                                          T* __restrict__ summ,
+                                                          int32_t* __restrict__ ctx) {
+  const int b = blockIdx.x;
+  const int t = ctx[b];
+  const bool ok = t >= 0 && t < sh.NBmax * kBlock;
+  if (ok) {
+    const int j = t / kBlock, u = t % kBlock;
+    for (int i = threadIdx.x; i < sh.H * D; i += kThreads) {
+      const int h = i / D, c = i % D;
+      const size_t unit = (size_t)b * sh.H + h;
+      const T kv = k_new[unit * D + c];
+      const T vv = v_new[unit * D + c];
+      T* r = rec + (unit * sh.NBmax + j) * (2 * kBlock * D);
+      r[u * D + c] = kv;
+      r[kBlock * D + c * kBlock + u] = vv;
+      if (pool) {
+        const int s = l2p[unit * sh.NBmax + j];
+        if (s >= 0 && s < sh.K) {
+          T* p = pool + (unit * sh.K + s) * (2 * kBlock * D);
+          p[u * D + c] = kv;
+          p[kBlock * D + c * kBlock + u] = vv;
+        }
+      }
+      T* sm = summ + (unit * sh.NBmax + j) * 2 * D + c;
+      if (u == 0) {
+        sm[0] = kv;
+        sm[D] = kv;
+      } else {
+        const float x = elem_f32(kv);
+        if (x < elem_f32(sm[0])) sm[0] = kv;
+        if (x > elem_f32(sm[D])) sm[D] = kv;
+      }
+    }
+  }
+  __syncthreads();
+  if (ok && threadIdx.x == 0) ctx[b] = t + 1;
+}
+
 // ------------------------------------------------------------------ fused layer step
 // Every unit runs attention (the resident blocks) and the summary scan +
 // top-K; only the eviction must come after both (it rewrites the slot map that
@@ -516,6 +571,24 @@ hipError_t launch_evict(const Shape& sh, const int32_t* topk_idx, int step, int 
   const size_t lds = SelectLds(0, sh.K).total;
   hipLaunchKernelGGL(evict_kernel, dim3(sh.B * sh.H), dim3(kThreads), lds, st, sh, topk_idx, step,
                      max_admit, l2p, p2l, last_sel, admit, admit_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Shape& sh, int dtype, const void* k_new, const void* v_new,
+                         void* records, void* pool, const int32_t* l2p, void* summ,
+                         int32_t* ctx, hipStream_t st) {
+  dim3 grid(sh.B);
+  if (dtype == 1) {
+    auto* f = sh.d == 128 ? append_kernel<uint16_t, 128> : append_kernel<uint16_t, 64>;
+    hipLaunchKernelGGL(f, grid, dim3(kThreads), 0, st, sh, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, (uint16_t*)records, (uint16_t*)pool, l2p,
+                       (uint16_t*)summ, ctx);
+  } else {
+    auto* f = sh.d == 128 ? append_kernel<float, 128> : append_kernel<float, 64>;
+    hipLaunchKernelGGL(f, grid, dim3(kThreads), 0, st, sh, (const float*)k_new,
+                       (const float*)v_new, (float*)records, (float*)pool, l2p, (float*)summ,
+                       ctx);
+  }
   return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ hipError_t launch_evict(const Shape& sh, const int32_t* topk_idx, int step, int 
 hipError_t launch_prefetch_gather(const Shape& sh, size_t rec_bytes, const void* records,
                                   void* pool, const int32_t* admit, const int32_t* admit_count,
                                   int max_admit, hipStream_t st);
+hipError_t launch_append(const Shape& sh, int dtype, const void* k_new, const void* v_new,
+                         void* records, void* pool, const int32_t* l2p, void* summ,
+                         int32_t* ctx_len, hipStream_t st);
 hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const void* pool,
                              const void* summ, const int32_t* ctx_len, float scale, int step,
                              int max_admit, void* out, int32_t* topk_idx, float* topk_score,

@@ -117,6 +117,20 @@ def records(cfg: Config, ctx: np.ndarray, nbmax: int, seed: Optional[int] = None
     return out
 
 
+def new_tokens(cfg: Config, n: int, seed: int, device="cpu", integer: bool = False):
+    """Keys and values of n decode steps' new tokens, each [n][B][Hkv][d] in the
+    storage dtype: N(0, 1) like the records, or small integers in [-3, 3]
+    (frequent ties, for the summary tie rule)."""
+    B, H, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    g = _gen(device, seed * 7919 + 11)
+    if integer:
+        kv = torch.randint(-3, 4, (2, n, B, H, d), generator=g, device=device).to(torch.float32)
+    else:
+        kv = torch.randn((2, n, B, H, d), generator=g, device=device)
+    kv = kv.to(TORCH_DTYPE[cfg.dtype])
+    return kv[0].contiguous(), kv[1].contiguous()
+
+
 def empty_state(cfg: Config, nbmax: int, device="cpu"):
     """(l2p [B][Hkv][NBmax], p2l [B][Hkv][K], last_sel [B][Hkv][K]), all int32."""
     B, H, K = cfg.batch, cfg.n_kv_heads, cfg.k_resident

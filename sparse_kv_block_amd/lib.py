@@ -28,7 +28,8 @@ SYMBOLS = ("oasis_abi_version", "oasis_last_error", "oasis_cap_to_max_admit",
            "oasis_record_bytes", "oasis_summary_bytes", "oasis_host_to_device_ptr",
            "oasis_summarize", "oasis_lookahead_attn", "oasis_score_topk",
            "oasis_capped_evict", "oasis_prefetch", "oasis_layer_step",
-           "oasis_layer_step_workspace_bytes", "oasis_dense_attn", "oasis_dense_attn_workspace_bytes")
+           "oasis_layer_step_workspace_bytes", "oasis_dense_attn", "oasis_dense_attn_workspace_bytes",
+           "oasis_append_token")
 
 
 class OasisError(RuntimeError):
@@ -83,6 +84,7 @@ def _load():
         "oasis_layer_step_workspace_bytes": ([SP], ctypes.c_size_t),
         "oasis_dense_attn": ([SP, P, P, P, F, P, P, ctypes.c_size_t, P], I32),
         "oasis_dense_attn_workspace_bytes": ([SP], ctypes.c_size_t),
+        "oasis_append_token": ([SP, P, P, P, P, P, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -160,6 +162,21 @@ def summarize(shape: Shape, records, ctx_len, summ, stream=None):
     _check(_lib.oasis_summarize(
         ctypes.byref(shape), _any(records, "records", dt, U * NB * shape.record_elems()),
         _dev(ctx_len, "ctx_len", I32, shape.batch), _dev(summ, "summ", dt, U * NB * 2 * d),
+        _stream(stream)))
+
+
+def append_token(shape: Shape, k_new, v_new, records, summ, ctx_len, pool=None, l2p=None,
+                 stream=None):
+    """Decode append of one token per request (see oasis_append_token)."""
+    dt, U, NB, d = shape.torch_dtype(), shape.units(), shape.max_blocks, shape.head_dim
+    if (pool is None) != (l2p is None):
+        raise ValueError("pool and l2p must both be given or both be None")
+    pp = None if pool is None else _dev(pool, "pool", dt, U * shape.k_resident * shape.record_elems())
+    lp = None if l2p is None else _dev(l2p, "l2p", I32, U * NB)
+    _check(_lib.oasis_append_token(
+        ctypes.byref(shape), _dev(k_new, "k_new", dt, U * d), _dev(v_new, "v_new", dt, U * d),
+        _any(records, "records", dt, U * NB * shape.record_elems()), pp, lp,
+        _dev(summ, "summ", dt, U * NB * 2 * d), _dev(ctx_len, "ctx_len", I32, shape.batch),
         _stream(stream)))
 
 

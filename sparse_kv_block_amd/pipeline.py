@@ -3,8 +3,8 @@
 `Layer` owns the HBM side of the look-ahead decode step for one layer: the
 resident slot pool, the block summaries, the per-KV-head block maps and the
 per-step outputs.  The full KV (records) lives elsewhere (pinned host memory
-or device memory) and is only read through `summarize`, `cold_fill` and
-`prefetch`.  Every method enqueues C-ABI calls on the current stream.
+or device memory) and is read through `summarize`, `cold_fill` and `prefetch`
+and written by `append`.  Every method enqueues C-ABI calls on the current stream.
 """
 from __future__ import annotations
 
@@ -54,6 +54,13 @@ class Layer:
         lib.capped_evict(self.shape, self.topk_idx, 0, K, self.l2p, self.p2l, self.last_sel,
                          self.admit, self.admit_count)
         self.prefetch(records, K, mode=mode, host_staging=host_staging)
+
+    def append(self, records, k_new: torch.Tensor, v_new: torch.Tensor):
+        """Decode append of one token per request ([B][Hkv][d] keys and values):
+        into `records`, the resident copy of its block when resident, and the
+        block's summary; this layer's context lengths grow by one."""
+        lib.append_token(self.shape, k_new, v_new, records, self.summ, self.ctx_len,
+                         pool=self.pool, l2p=self.l2p)
 
     def set_state(self, l2p, p2l, last_sel):
         self.l2p.copy_(torch.as_tensor(l2p))

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_helpers(L, ora):
     raw = L.raw()
-    assert raw.oasis_abi_version() == 3
+    assert raw.oasis_abi_version() == 4
     for cap, K in [(0.0, 128), (0.01, 128), (0.05, 128), (0.2, 128), (1.0, 128), (0.25, 8),
                    (2.0, 16), (-1.0, 8), (0.3, 10), (0.7, 10)]:
         assert L.cap_to_max_admit(cap, K) == ora.max_admit(cap, K), (cap, K)
@@ -88,12 +88,17 @@ def test_null_pointers_and_bad_scalars(L):
     assert raw.oasis_prefetch(ctypes.byref(s), p, p, p, p, 6, L.MEMCPY, None, None, None,
                               None) == L.ERR_INVALID
     assert "host_staging" in L.last_error()
+    assert raw.oasis_append_token(ctypes.byref(s), p, p, p, p, None, p, p, None) == L.ERR_INVALID
+    assert "both" in L.last_error()
+    assert raw.oasis_append_token(ctypes.byref(s), p, p, None, None, None, p, p, None) == L.ERR_INVALID
+    assert "records is NULL" in L.last_error()
 
 
 def test_empty_batch_is_a_no_op(L):
     raw = L.raw()
     s = shape(batch=0)
     assert raw.oasis_summarize(ctypes.byref(s), None, None, None, None) == L.OK
+    assert raw.oasis_append_token(ctypes.byref(s), *([None] * 7), None) == L.OK
     assert raw.oasis_layer_step(ctypes.byref(s), *([None] * 4), 0.0, 1, 6, *([None] * 8), None, 0,
                                 None) == L.OK
 
