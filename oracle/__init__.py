@@ -48,8 +48,9 @@ def lib():
         L.ora_attention.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, D, P, P, I, I]
         L.ora_prefetch.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, I]
         L.ora_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
+        L.ora_exact_block_scores.argtypes = [I, I, I, I, I, I, I, P, I, P, P, P, P, I, I]
         for f in (L.ora_summarize, L.ora_block_scores, L.ora_topk, L.ora_capped_evict,
-                  L.ora_attention, L.ora_prefetch, L.ora_append):
+                  L.ora_attention, L.ora_prefetch, L.ora_append, L.ora_exact_block_scores):
             f.restype = None
         _lib = L
     return _lib
@@ -131,6 +132,47 @@ def block_scores(q, summ, ctx_len, block_size: int, q_row: int = 1, units=None,
                            _ptr(sa), _ptr(ctx), _ptr(scores), _ptr(u), nu,
                            nthreads or default_threads())
     return scores
+
+
+def exact_block_scores(q, records, ctx_len, block_size: int, q_row: int = 0, units=None,
+                       nthreads=None, scores=None):
+    """Exact block scores from the keys: sum over the KV head's query heads of
+    the largest logit over the block's valid tokens ([B][H][NBmax], -inf past
+    the context)."""
+    qa, rec = as_np(q), as_np(records)
+    B, H, NB, E = rec.shape
+    d = E // (2 * block_size)
+    Hq = qa.shape[2]
+    ctx = np.ascontiguousarray(as_np(ctx_len).astype(np.int32))
+    if scores is None:
+        scores = np.full((B, H, NB), np.nan, dtype=np.float64)
+    u, nu = _units(units)
+    lib().ora_exact_block_scores(B, Hq, H, NB, block_size, d, dtype_code(rec), _ptr(qa), q_row,
+                                 _ptr(rec), _ptr(ctx), _ptr(scores), _ptr(u), nu,
+                                 nthreads or default_threads())
+    return scores
+
+
+def agreement(pred_idx, exact_idx, l2p=None):
+    """Per unit (n_exact, |pred & exact|, |exact & resident|): the exact top-K
+    list's valid entries, how many of them the predicted list holds, and how
+    many are resident by the slot map l2p (-1 where l2p is None)."""
+    P = np.asarray(as_np(pred_idx), np.int64)
+    X = np.asarray(as_np(exact_idx), np.int64)
+    B, H, K = X.shape
+    out = np.zeros((B, H, 3), np.int32)
+    for b in range(B):
+        for h in range(H):
+            ex = {int(j) for j in X[b, h] if j >= 0}
+            pr = {int(j) for j in P[b, h] if j >= 0}
+            out[b, h, 0] = len(ex)
+            out[b, h, 1] = len(ex & pr)
+            if l2p is None:
+                out[b, h, 2] = -1
+            else:
+                lp = as_np(l2p)[b, h]
+                out[b, h, 2] = sum(1 for j in ex if lp[j] >= 0)
+    return out
 
 
 def topk(scores, ctx_len, block_size: int, K: int, units=None, idx=None, val=None):

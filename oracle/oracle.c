@@ -171,6 +171,62 @@ void ora_block_scores(int B, int Hq, int H, int NBmax, int S, int d, int dtype,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Exact block scores, the ground truth the draft's prediction is compared
+ * with (pith.science paper page, "Core claim" and the referee report on
+ * Fig. 6: the propagated draft query's top-K set against the exact top-K set
+ * of the true next-token query).  Per query head the exact score of a block
+ * is the largest logit q . k_t over its valid tokens t; the G query heads of
+ * the KV head are summed, exactly as the Quest bounds are summed, so that the
+ * bound is never below it.  Blocks past the context get -inf.              */
+
+typedef struct {
+    int Hq, H, NBmax, S, d, dtype, q_row;
+    const void* q;
+    const void* rec;
+    const int32_t* ctx_len;
+    double* scores;
+} exact_ctx;
+
+static void exact_unit(void* p, int unit) {
+    exact_ctx* c = (exact_ctx*)p;
+    int b = unit / c->H, h = unit % c->H;
+    int G = c->Hq / c->H;
+    int32_t L = c->ctx_len[b];
+    int nb = n_blocks(L, c->S, c->NBmax);
+    size_t rec_elems = (size_t)2 * c->S * c->d;
+    for (int j = 0; j < c->NBmax; ++j) {
+        double s = -INFINITY;
+        if (j < nb) {
+            size_t rbase = ((size_t)unit * c->NBmax + j) * rec_elems;
+            int nvalid = L - j * c->S;
+            if (nvalid > c->S) nvalid = c->S;
+            s = 0.0;
+            for (int i = h * G; i < (h + 1) * G; ++i) {
+                size_t qbase = (((size_t)b * 2 + c->q_row) * c->Hq + i) * (size_t)c->d;
+                double best = -INFINITY;
+                for (int u = 0; u < nvalid; ++u) {
+                    double logit = 0.0;
+                    for (int ch = 0; ch < c->d; ++ch)
+                        logit += elem(c->q, c->dtype, qbase + ch) *
+                                 elem(c->rec, c->dtype, rbase + (size_t)u * c->d + ch);
+                    if (logit > best) best = logit;
+                }
+                s += best;
+            }
+        }
+        c->scores[(size_t)unit * c->NBmax + j] = s;
+    }
+}
+
+void ora_exact_block_scores(int B, int Hq, int H, int NBmax, int S, int d, int dtype,
+                            const void* q, int q_row, const void* records,
+                            const int32_t* ctx_len, double* scores,
+                            const int32_t* units, int n_units, int nthreads) {
+    exact_ctx c = {Hq, H, NBmax, S, d, dtype, q_row, q, records, ctx_len, scores};
+    for_units(exact_unit, &c, units, units ? n_units : B * H, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Top-K: the K best blocks of the unit by (score descending, block index
  * ascending), listed in that order; all blocks if the request has at most K.
  * Unused entries are index -1, score -inf.                                   */

@@ -51,6 +51,14 @@ void ora_block_scores(int B, int Hq, int H, int NBmax, int S, int d, int dtype,
                       const int32_t* ctx_len, double* scores,
                       const int32_t* units, int n_units, int nthreads);
 
+/* Exact block scores (ground truth of the top-K agreement diagnostic): per
+ * block, the sum over the G query heads of the largest logit q_i . k_t over
+ * the block's valid tokens (keys read from `records`). */
+void ora_exact_block_scores(int B, int Hq, int H, int NBmax, int S, int d, int dtype,
+                            const void* q, int q_row, const void* records,
+                            const int32_t* ctx_len, double* scores,
+                            const int32_t* units, int n_units, int nthreads);
+
 void ora_topk(int B, int H, int NBmax, int S, int K, const double* scores,
               const int32_t* ctx_len, int32_t* topk_idx, double* topk_score,
               const int32_t* units, int n_units);

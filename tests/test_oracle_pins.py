@@ -425,3 +425,78 @@ def test_append_places_tokens_and_keeps_summaries_exact(ora, dtype):
     np.testing.assert_array_equal(ora.to_f64(summ), ora.to_f64(ora.summarize(rec, ctx, S)))
     np.testing.assert_array_equal(pool[2, 1, 2], rec[2, 1, 3])
     assert ctx.tolist() == [19, 14, 24]            # request 2 stopped at capacity
+
+
+# --------------------------------------------------------------------------
+# Exact block scores and top-K agreement (the diagnostic's ground truth)
+def test_exact_score_worked_example(ora):
+    g = json.load(open(os.path.join(GOLDEN, "exact_score_worked_example.json")))
+    S, d = g["block_size"], g["head_dim"]
+    keys = np.array(g["keys_by_token"], np.float32)
+    NB = keys.shape[0] // S
+    rec = np.zeros((1, 1, NB, 2 * S * d), np.float32)
+    for j in range(NB):
+        rec[0, 0, j, : S * d] = keys[j * S:(j + 1) * S].reshape(-1)
+    ctx = np.array([g["ctx_len"]], np.int32)
+    q = np.full((1, 2, g["n_q_heads"], d), 50.0, np.float32)      # row 1 must not matter
+    q[0, 0] = np.array(g["q_by_head"], np.float32)
+    ex = ora.exact_block_scores(q, rec, ctx, S, q_row=0)
+    np.testing.assert_array_equal(ex[0, 0], np.array(g["exact_scores"], np.float64))
+    summ = ora.summarize(rec, ctx, S)
+    qs = ora.block_scores(q, summ, ctx, S, q_row=0)
+    np.testing.assert_array_equal(qs[0, 0], np.array(g["quest_scores"], np.float64))
+    idx, _ = ora.topk(ex, ctx, S, 1)
+    assert idx[0, 0].tolist() == g["top1"]
+    # the other query row is read when asked for
+    q2 = q[:, ::-1].copy()
+    np.testing.assert_array_equal(ora.exact_block_scores(q2, rec, ctx, S, q_row=1), ex)
+
+
+def test_exact_scores_equal_the_bound_for_one_token_blocks(ora):
+    # With S = 1 a block's min and max are its key, so the Quest bound is exact
+    # and the two independently computed scores must coincide.
+    cfg = tiny(block_size=1, ctx=41, n_q_heads=6, n_kv_heads=2, head_dim=8, batch=3)
+    ctx, nbmax, rec, q = make(cfg, ctx=[41, 7, 0], seed=8)
+    summ = ora.summarize(rec, ctx, 1)
+    for row in (0, 1):
+        ex = ora.exact_block_scores(q, rec, ctx, 1, q_row=row)
+        qs = ora.block_scores(q, summ, ctx, 1, q_row=row)
+        np.testing.assert_allclose(ex, qs, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_exact_scores_never_exceed_the_bound(ora, dtype):
+    cfg = tiny(dtype=dtype, n_q_heads=8, n_kv_heads=2, head_dim=16, ctx=333, batch=2)
+    ctx, nbmax, rec, q = make(cfg, ctx=[333, 100], seed=9)
+    summ = ora.summarize(rec, ctx, cfg.block_size)
+    ex = ora.exact_block_scores(q, rec, ctx, cfg.block_size, q_row=1)
+    qs = ora.block_scores(q, summ, ctx, cfg.block_size, q_row=1)
+    fin = np.isfinite(qs)
+    assert np.array_equal(fin, np.isfinite(ex))
+    assert np.all(ex[fin] <= qs[fin] + 1e-9 * (1 + np.abs(qs[fin])))
+    # and the bound is not trivially loose: some block comes within 30 %
+    assert np.any(ex[fin] > 0.7 * qs[fin])
+
+
+def test_exact_scores_ignore_token_order_and_duplicates(ora):
+    # The max over a block's tokens does not depend on their order, and
+    # replacing a token by a copy of another token of the block cannot raise it.
+    cfg = tiny(head_dim=8, ctx=64, n_q_heads=4, n_kv_heads=1, batch=1)
+    ctx, nbmax, rec, q = make(cfg, seed=10)
+    S, d = cfg.block_size, cfg.head_dim
+    ex = ora.exact_block_scores(q, rec, ctx, S, q_row=0)
+    r = ora.as_np(rec).copy()
+    k = r[..., : S * d].reshape(1, 1, nbmax, S, d)
+    k[:] = k[:, :, :, ::-1].copy()
+    np.testing.assert_allclose(ora.exact_block_scores(q, r, ctx, S, q_row=0), ex, rtol=1e-12)
+    k[:, :, :, 0] = k[:, :, :, 1]
+    assert np.all(ora.exact_block_scores(q, r, ctx, S, q_row=0) <= ex + 1e-12)
+
+
+def test_agreement_counts(ora):
+    pred = np.array([[[0, 2, 5, -1]]], np.int32)
+    exact = np.array([[[2, 3, 5, -1]]], np.int32)
+    l2p = np.full((1, 1, 8), -1, np.int32)
+    l2p[0, 0, [3, 5, 7]] = [0, 1, 2]
+    assert ora.agreement(pred, exact, l2p)[0, 0].tolist() == [3, 2, 2]
+    assert ora.agreement(exact, exact)[0, 0].tolist() == [3, 3, -1]
