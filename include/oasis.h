@@ -215,6 +215,34 @@ oasis_status oasis_append_token(const oasis_shape* shape, const void* k_new,
                                 const int32_t* l2p, void* summ,
                                 int32_t* ctx_len, void* stream);
 
+/* Top-K agreement diagnostic (a synthetic stand-in for the pith.science
+ * paper page's "Core claim" measurement and the referee report on its
+ * Fig. 6: the draft query's predicted top-K set against the exact top-K set
+ * of the true next query).
+ *
+ * oasis_exact_topk: exact block scores from the keys, then the same top-K as
+ * oasis_score_topk (same outputs, order and tie rule).  The exact score of
+ * block j of unit (b, h) for query row q_row is the sum over the unit's G
+ * query heads i of max over the block's valid tokens t of q_i . k_t
+ * (unscaled): the quantity the summed Quest bounds of oasis_score_topk bound
+ * from above.  `records` is the full KV [B][Hkv][NBmax][record] (device
+ * memory; host-mapped memory works but reads over the host link).
+ *
+ * oasis_topk_agreement: per unit, counts[b][h][0] = entries of exact_idx in
+ * [0, NBmax), [1] = how many of those pred_idx also lists, [2] = how many of
+ * those are resident by l2p (l2p[b][h][j] >= 0), or -1 when l2p is NULL.
+ * pred_idx, exact_idx [B][Hkv][K] int32 lists of distinct blocks (-1 =
+ * unused); counts [B][Hkv][3] int32; all device memory. */
+oasis_status oasis_exact_topk(const oasis_shape* shape, const void* q,
+                              int32_t q_row, const void* records,
+                              const int32_t* ctx_len, int32_t* topk_idx,
+                              float* topk_score, void* stream);
+oasis_status oasis_topk_agreement(const oasis_shape* shape,
+                                  const int32_t* pred_idx,
+                                  const int32_t* exact_idx,
+                                  const int32_t* l2p, int32_t* counts,
+                                  void* stream);
+
 /* Workspace bytes oasis_layer_step needs for a shape: 0 while
  * max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K lists
  * of the split summary scan and one counter per unit). */

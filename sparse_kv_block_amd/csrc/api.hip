@@ -86,7 +86,7 @@ size_t esize(const oasis_shape* s) { return s->dtype == OASIS_DTYPE_F32 ? 4 : 2;
 
 extern "C" {
 
-int32_t oasis_abi_version(void) { return 4; }
+int32_t oasis_abi_version(void) { return 5; }
 
 const char* oasis_last_error(void) { return g_error.c_str(); }
 
@@ -268,6 +268,37 @@ oasis_status oasis_append_token(const oasis_shape* shape, const void* k_new, con
     return fail(OASIS_ERR_INVALID, "%s: pool and l2p must both be given or both be NULL", fn);
   return hip_status(oasis::launch_append(to_shape(shape), shape->dtype, k_new, v_new, records, pool,
                                          l2p, summ, ctx_len, (hipStream_t)stream),
+                    fn);
+}
+
+oasis_status oasis_exact_topk(const oasis_shape* shape, const void* q, int32_t q_row,
+                              const void* records, const int32_t* ctx_len, int32_t* topk_idx,
+                              float* topk_score, void* stream) {
+  const char* fn = "oasis_exact_topk";
+  if (oasis_status st = check_shape(shape, fn)) return st;
+  if (q_row != 0 && q_row != 1) return fail(OASIS_ERR_INVALID, "%s: q_row %d (0 or 1)", fn, q_row);
+  if (shape->batch == 0) return OASIS_OK;
+  OASIS_NONNULL(q, fn);
+  OASIS_NONNULL(records, fn);
+  OASIS_NONNULL(ctx_len, fn);
+  OASIS_NONNULL(topk_idx, fn);
+  OASIS_NONNULL(topk_score, fn);
+  return hip_status(oasis::launch_exact_topk(to_shape(shape), shape->dtype, q, q_row, records,
+                                             ctx_len, topk_idx, topk_score, (hipStream_t)stream),
+                    fn);
+}
+
+oasis_status oasis_topk_agreement(const oasis_shape* shape, const int32_t* pred_idx,
+                                  const int32_t* exact_idx, const int32_t* l2p, int32_t* counts,
+                                  void* stream) {
+  const char* fn = "oasis_topk_agreement";
+  if (oasis_status st = check_shape(shape, fn)) return st;
+  if (shape->batch == 0) return OASIS_OK;
+  OASIS_NONNULL(pred_idx, fn);
+  OASIS_NONNULL(exact_idx, fn);
+  OASIS_NONNULL(counts, fn);
+  return hip_status(oasis::launch_agreement(to_shape(shape), pred_idx, exact_idx, l2p, counts,
+                                            (hipStream_t)stream),
                     fn);
 }
 

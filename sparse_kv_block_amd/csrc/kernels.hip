@@ -6,6 +6,7 @@
 // synchronisation.  At batch 128 x 8 KV heads that is 1024 workgroups, four
 // per CU on the 256 CUs, all resident at once.
 #include "attn_dev.h"
+#include "diag_dev.h"
 #include "launch.h"
 #include "select_dev.h"
 #include "step_dev.h"
@@ -121,6 +122,20 @@ __device__ __forceinline__ SelectPtrs select_ptrs(char* smem, int NBmax, int K) 
   return p;
 }
 
+// Top-K of the scores in p.keys[0..nb); leaves the sorted list in p.sel_idx
+// (entries past kk set to -1) and writes the top-K outputs of the unit.
+__device__ __forceinline__ void select_from_keys(const Shape& sh, int unit, int nb,
+                                                 int32_t* topk_idx, float* topk_score,
+                                                 const SelectPtrs& p) {
+  const int kk = topk_unit(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  for (int t = threadIdx.x; t < sh.K; t += kThreads) {
+    if (t >= kk) p.sel_idx[t] = -1;
+    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
+    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
+  }
+  __syncthreads();
+}
+
 // Scan + select for one unit; leaves the sorted list in p.sel_idx (entries
 // past kk set to -1) and writes the top-K outputs.
 template <typename T, int D, int U>
@@ -131,13 +146,7 @@ __device__ __forceinline__ void select_unit(const Shape& sh, const T* q, int q_r
   const int nb = n_blocks(L, sh.NBmax);
   scan_unit<T, D, U>(sh, q, q_row, summ + (size_t)unit * sh.NBmax * 2 * D, b, h, nb, p.keys);
   __syncthreads();
-  const int kk = topk_unit(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
-  for (int t = threadIdx.x; t < sh.K; t += kThreads) {
-    if (t >= kk) p.sel_idx[t] = -1;
-    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
-    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
-  }
-  __syncthreads();
+  select_from_keys(sh, unit, nb, topk_idx, topk_score, p);
 }
 
 template <typename T, int D>
@@ -150,6 +159,65 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T*
   const int unit = blockIdx.x;
   const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
   select_unit<T, D, 4>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
+}
+
+// ------------------------------------------------------------------ agreement diagnostic
+// Exact block scores of one unit from its keys in the full KV, then the same
+// top-K as the summary scan's.
+constexpr int kExactInFlight = 4;   // blocks per wave in flight (bf16)
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void exact_topk_kernel(Shape sh, const T* __restrict__ q,
+                                                              int q_row, const T* __restrict__ rec,
+                                                              const int32_t* __restrict__ ctx,
+                                                              int32_t* __restrict__ topk_idx,
+                                                              float* __restrict__ topk_score) {
+  extern __shared__ __align__(16) char smem[];
+  const int unit = blockIdx.x;
+  const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
+  const int b = unit / sh.H, h = unit % sh.H;
+  const int L = ctx[b];
+  const int nb = n_blocks(L, sh.NBmax);
+  const T* rec_unit = rec + (size_t)unit * sh.NBmax * (2 * kBlock * D);
+  if constexpr (sizeof(T) == 2)
+    exact_scan_bf16<D, kExactInFlight>(sh, q, q_row, rec_unit, b, h, L, nb, p.keys);
+  else
+    exact_scan_f32<D>(sh, q, q_row, rec_unit, b, h, L, nb, p.keys);
+  __syncthreads();
+  select_from_keys(sh, unit, nb, topk_idx, topk_score, p);
+}
+
+// Per unit: entries of the exact list in [0, NBmax), how many of them the
+// predicted list holds, and how many are resident by the slot map (-1 without
+// a map).  A bitmap of the predicted blocks lives in LDS; one list entry per
+// thread (K <= 256).
+__global__ __launch_bounds__(kThreads) void agreement_kernel(Shape sh, const int32_t* __restrict__ pred,
+                                                             const int32_t* __restrict__ exact,
+                                                             const int32_t* __restrict__ l2p,
+                                                             int32_t* __restrict__ counts) {
+  __shared__ uint32_t bits[8192 / 32];
+  const int unit = blockIdx.x;
+  const int words = (sh.NBmax + 31) / 32;
+  for (int i = threadIdx.x; i < words; i += kThreads) bits[i] = 0u;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < sh.K) {
+    const int j = pred[(size_t)unit * sh.K + t];
+    if (j >= 0 && j < sh.NBmax) atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  int j = t < sh.K ? exact[(size_t)unit * sh.K + t] : -1;
+  const bool valid = j >= 0 && j < sh.NBmax;
+  const bool agree = valid && ((bits[j >> 5] >> (j & 31)) & 1u);
+  const bool res = valid && l2p && l2p[(size_t)unit * sh.NBmax + j] >= 0;
+  const int n_valid = __syncthreads_count(valid);
+  const int n_agree = __syncthreads_count(agree);
+  const int n_res = __syncthreads_count(res);
+  if (t == 0) {
+    counts[(size_t)unit * 3 + 0] = n_valid;
+    counts[(size_t)unit * 3 + 1] = n_agree;
+    counts[(size_t)unit * 3 + 2] = l2p ? n_res : -1;
+  }
 }
 
 // ------------------------------------------------------------------ eviction
@@ -562,6 +630,27 @@ hipError_t launch_score_topk(const Shape& sh, int dtype, const void* q, int q_ro
   if (dtype == 1) { if (sh.d == 128) OASIS_SCORE(uint16_t, 128); else OASIS_SCORE(uint16_t, 64); }
   else            { if (sh.d == 128) OASIS_SCORE(float, 128);    else OASIS_SCORE(float, 64); }
 #undef OASIS_SCORE
+  return hipGetLastError();
+}
+
+hipError_t launch_exact_topk(const Shape& sh, int dtype, const void* q, int q_row,
+                             const void* records, const int32_t* ctx, int32_t* topk_idx,
+                             float* topk_score, hipStream_t st) {
+  dim3 grid(sh.B * sh.H);
+  const size_t lds = SelectLds(sh.NBmax, sh.K).total;
+#define OASIS_EXACT(T_, D_)                                                                   \
+  hipLaunchKernelGGL((exact_topk_kernel<T_, D_>), grid, dim3(kThreads), lds, st, sh,          \
+                     (const T_*)q, q_row, (const T_*)records, ctx, topk_idx, topk_score)
+  if (dtype == 1) { if (sh.d == 128) OASIS_EXACT(uint16_t, 128); else OASIS_EXACT(uint16_t, 64); }
+  else            { if (sh.d == 128) OASIS_EXACT(float, 128);    else OASIS_EXACT(float, 64); }
+#undef OASIS_EXACT
+  return hipGetLastError();
+}
+
+hipError_t launch_agreement(const Shape& sh, const int32_t* pred, const int32_t* exact,
+                            const int32_t* l2p, int32_t* counts, hipStream_t st) {
+  hipLaunchKernelGGL(agreement_kernel, dim3(sh.B * sh.H), dim3(kThreads), 0, st, sh, pred, exact,
+                     l2p, counts);
   return hipGetLastError();
 }
 

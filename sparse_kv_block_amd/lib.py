@@ -29,7 +29,7 @@ SYMBOLS = ("oasis_abi_version", "oasis_last_error", "oasis_cap_to_max_admit",
            "oasis_summarize", "oasis_lookahead_attn", "oasis_score_topk",
            "oasis_capped_evict", "oasis_prefetch", "oasis_layer_step",
            "oasis_layer_step_workspace_bytes", "oasis_dense_attn", "oasis_dense_attn_workspace_bytes",
-           "oasis_append_token")
+           "oasis_append_token", "oasis_exact_topk", "oasis_topk_agreement")
 
 
 class OasisError(RuntimeError):
@@ -85,6 +85,8 @@ def _load():
         "oasis_dense_attn": ([SP, P, P, P, F, P, P, ctypes.c_size_t, P], I32),
         "oasis_dense_attn_workspace_bytes": ([SP], ctypes.c_size_t),
         "oasis_append_token": ([SP, P, P, P, P, P, P, P, P], I32),
+        "oasis_exact_topk": ([SP, P, I32, P, P, P, P, P], I32),
+        "oasis_topk_agreement": ([SP, P, P, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -196,6 +198,27 @@ def score_topk(shape: Shape, q, summ, ctx_len, topk_idx, topk_score, q_row: int 
         _dev(summ, "summ", dt, U * shape.max_blocks * 2 * d),
         _dev(ctx_len, "ctx_len", I32, shape.batch), _dev(topk_idx, "topk_idx", I32, U * K),
         _dev(topk_score, "topk_score", torch.float32, U * K), _stream(stream)))
+
+
+def exact_topk(shape: Shape, q, records, ctx_len, topk_idx, topk_score, q_row: int = 0,
+               stream=None):
+    """Top-K of the exact block scores (see oasis_exact_topk)."""
+    dt, U, K, d = shape.torch_dtype(), shape.units(), shape.k_resident, shape.head_dim
+    _check(_lib.oasis_exact_topk(
+        ctypes.byref(shape), _dev(q, "q", dt, shape.batch * 2 * shape.n_q_heads * d), int(q_row),
+        _any(records, "records", dt, U * shape.max_blocks * shape.record_elems()),
+        _dev(ctx_len, "ctx_len", I32, shape.batch), _dev(topk_idx, "topk_idx", I32, U * K),
+        _dev(topk_score, "topk_score", torch.float32, U * K), _stream(stream)))
+
+
+def topk_agreement(shape: Shape, pred_idx, exact_idx, counts, l2p=None, stream=None):
+    """Per-unit (n_exact, agreeing, resident) counts (see oasis_topk_agreement)."""
+    U, K = shape.units(), shape.k_resident
+    lp = None if l2p is None else _dev(l2p, "l2p", I32, U * shape.max_blocks)
+    _check(_lib.oasis_topk_agreement(
+        ctypes.byref(shape), _dev(pred_idx, "pred_idx", I32, U * K),
+        _dev(exact_idx, "exact_idx", I32, U * K), lp, _dev(counts, "counts", I32, U * 3),
+        _stream(stream)))
 
 
 def capped_evict(shape: Shape, topk_idx, step: int, max_admit: int, l2p, p2l, last_sel, admit,
