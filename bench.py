@@ -147,6 +147,64 @@ def append_leg(layer, rec_host, reps: int = 8):
     return res
 
 
+def agreement_leg(cfg, ctx, nbmax, steps: int, caps, sigmas):
+    """Top-K agreement study on device-resident records (see
+    sparse_kv_block_amd.diagnostics): by fetch cap at the workload's draft
+    noise, and by draft noise at the workload's cap.  Also times one exact
+    top-K launch (the scan of every key of the batch)."""
+    import torch
+    from sparse_kv_block_amd import gen, lib
+    from sparse_kv_block_amd.diagnostics import run_study
+    from sparse_kv_block_amd.pipeline import Layer
+    dev = "cuda"
+    qseq = gen.query_sequence(cfg, steps + 3, device=dev)
+    dirs = gen.planted_directions(cfg, qseq[1]) if cfg.planted else None
+    rec = gen.records(cfg, ctx, nbmax, device=dev, planted_dir=dirs)
+    out = {"steps": steps, "draft_sigma": cfg.draft_sigma, "cap": cfg.cap, "by_cap": {},
+           "by_sigma": {}}
+
+    def one(c, cap):
+        qs = [None] + [gen.step_queries(c, qseq, s) for s in range(1, steps + 2)]
+        layer = Layer(c, ctx, nbmax, device=dev)
+        layer.summarize(rec)
+        layer.cold_fill(qs[1], rec)
+        res = run_study(layer, rec, qs, steps, max_admit=lib.cap_to_max_admit(cap, c.k_resident))
+        del layer
+        return res, qs
+
+    for cap in caps:
+        out["by_cap"][str(cap)], qs = one(cfg, cap)
+        log(f"[bench] agreement cap {cap}: {out['by_cap'][str(cap)]}")
+    for sg in sigmas:
+        out["by_sigma"][str(sg)], _ = one(cfg.scaled(draft_sigma=sg), cfg.cap)
+        log(f"[bench] agreement sigma {sg}: {out['by_sigma'][str(sg)]}")
+    # exact top-K timing
+    shape = lib.Shape.of(cfg, nbmax)
+    ctx_d = torch.from_numpy(ctx).to(dev)
+    K = cfg.k_resident
+    idx = torch.empty((cfg.batch, cfg.n_kv_heads, K), dtype=torch.int32, device=dev)
+    sc = torch.empty((cfg.batch, cfg.n_kv_heads, K), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    lib.exact_topk(shape, qs[1], rec, ctx_d, idx, sc, q_row=1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(5)]
+    for a, b in ev:
+        a.record(stream)
+        lib.exact_topk(shape, qs[1], rec, ctx_d, idx, sc, q_row=1)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    es = 2 if cfg.dtype == "bf16" else 4
+    nb = np.minimum((ctx.astype(np.int64) + 15) // 16, nbmax)
+    key_bytes = int(nb.sum()) * cfg.n_kv_heads * 16 * cfg.head_dim * es
+    out["exact_topk"] = {"us": round(us, 1), "key_bytes": key_bytes,
+                         "GBps": round(key_bytes / (us * 1e-6) / 1e9, 1)}
+    log(f"[bench] exact top-K: {us:.1f} us over {key_bytes / 2**30:.2f} GiB of keys")
+    del rec
+    torch.cuda.empty_cache()
+    return out
+
+
 def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
     """The 36-layer decode step with the fetch-cap sweep: per layer the fused
     step on the main stream and the gather prefetch of its admissions on a side
@@ -239,6 +297,10 @@ def main():
                     help="also time the dense comparator (attention over the full HBM-resident KV)")
     ap.add_argument("--append", action="store_true",
                     help="also time the decode append (after every other GPU leg)")
+    ap.add_argument("--agreement", action="store_true",
+                    help="also run the top-K agreement study (after every other GPU leg; "
+                         "releases the timed layer's buffers)")
+    ap.add_argument("--agreement-steps", type=int, default=16)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, launch a plain elementwise copy of this many MiB "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -377,6 +439,11 @@ def main():
 
     if args.append:
         result["append"] = append_leg(layer, rec_host)
+    if args.agreement:
+        del layer
+        torch.cuda.empty_cache()
+        result["agreement"] = agreement_leg(cfg, ctx, nbmax, args.agreement_steps,
+                                            (0.01, 0.05, 0.2, 1.0), (0.0, 0.1, 0.2, 0.4))
 
     if not args.no_cpu_baseline:
         log(f"[bench] oracle baseline ...")

@@ -228,11 +228,13 @@ oasis_status oasis_append_token(const oasis_shape* shape, const void* k_new,
  * from above.  `records` is the full KV [B][Hkv][NBmax][record] (device
  * memory; host-mapped memory works but reads over the host link).
  *
- * oasis_topk_agreement: per unit, counts[b][h][0] = entries of exact_idx in
- * [0, NBmax), [1] = how many of those pred_idx also lists, [2] = how many of
- * those are resident by l2p (l2p[b][h][j] >= 0), or -1 when l2p is NULL.
- * pred_idx, exact_idx [B][Hkv][K] int32 lists of distinct blocks (-1 =
- * unused); counts [B][Hkv][3] int32; all device memory. */
+ * oasis_topk_agreement: per unit, counts[b][h][0] = entries among the first
+ * exact_n (1 <= exact_n <= K) of exact_idx that lie in [0, NBmax), [1] = how
+ * many of those pred_idx lists, [2] = how many of those are resident by l2p
+ * (l2p[b][h][j] >= 0), or -1 when l2p is NULL.  exact_n = K compares whole
+ * lists; a smaller exact_n asks for the recall of the exact list's best
+ * blocks.  pred_idx, exact_idx [B][Hkv][K] int32 lists of distinct blocks
+ * (-1 = unused); counts [B][Hkv][3] int32; all device memory. */
 oasis_status oasis_exact_topk(const oasis_shape* shape, const void* q,
                               int32_t q_row, const void* records,
                               const int32_t* ctx_len, int32_t* topk_idx,
@@ -240,8 +242,8 @@ oasis_status oasis_exact_topk(const oasis_shape* shape, const void* q,
 oasis_status oasis_topk_agreement(const oasis_shape* shape,
                                   const int32_t* pred_idx,
                                   const int32_t* exact_idx,
-                                  const int32_t* l2p, int32_t* counts,
-                                  void* stream);
+                                  const int32_t* l2p, int32_t exact_n,
+                                  int32_t* counts, void* stream);
 
 /* Workspace bytes oasis_layer_step needs for a shape: 0 while
  * max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K lists

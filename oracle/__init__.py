@@ -153,13 +153,16 @@ def exact_block_scores(q, records, ctx_len, block_size: int, q_row: int = 0, uni
     return scores
 
 
-def agreement(pred_idx, exact_idx, l2p=None):
-    """Per unit (n_exact, |pred & exact|, |exact & resident|): the exact top-K
-    list's valid entries, how many of them the predicted list holds, and how
-    many are resident by the slot map l2p (-1 where l2p is None)."""
+def agreement(pred_idx, exact_idx, l2p=None, exact_n=None):
+    """Per unit (n_exact, |pred & exact|, |exact & resident|) over the first
+    exact_n entries of the exact top-K list (all by default): its valid
+    entries, how many of them the predicted list holds, and how many are
+    resident by the slot map l2p (-1 where l2p is None)."""
     P = np.asarray(as_np(pred_idx), np.int64)
     X = np.asarray(as_np(exact_idx), np.int64)
-    B, H, K = X.shape
+    if exact_n is not None:
+        X = X[..., :exact_n]
+    B, H, _ = X.shape
     out = np.zeros((B, H, 3), np.int32)
     for b in range(B):
         for h in range(H):

@@ -86,7 +86,7 @@ size_t esize(const oasis_shape* s) { return s->dtype == OASIS_DTYPE_F32 ? 4 : 2;
 
 extern "C" {
 
-int32_t oasis_abi_version(void) { return 5; }
+int32_t oasis_abi_version(void) { return 6; }
 
 const char* oasis_last_error(void) { return g_error.c_str(); }
 
@@ -289,16 +289,18 @@ oasis_status oasis_exact_topk(const oasis_shape* shape, const void* q, int32_t q
 }
 
 oasis_status oasis_topk_agreement(const oasis_shape* shape, const int32_t* pred_idx,
-                                  const int32_t* exact_idx, const int32_t* l2p, int32_t* counts,
-                                  void* stream) {
+                                  const int32_t* exact_idx, const int32_t* l2p, int32_t exact_n,
+                                  int32_t* counts, void* stream) {
   const char* fn = "oasis_topk_agreement";
   if (oasis_status st = check_shape(shape, fn)) return st;
+  if (exact_n <= 0 || exact_n > shape->k_resident)
+    return fail(OASIS_ERR_INVALID, "%s: exact_n %d (1 .. K = %d)", fn, exact_n, shape->k_resident);
   if (shape->batch == 0) return OASIS_OK;
   OASIS_NONNULL(pred_idx, fn);
   OASIS_NONNULL(exact_idx, fn);
   OASIS_NONNULL(counts, fn);
-  return hip_status(oasis::launch_agreement(to_shape(shape), pred_idx, exact_idx, l2p, counts,
-                                            (hipStream_t)stream),
+  return hip_status(oasis::launch_agreement(to_shape(shape), pred_idx, exact_idx, l2p, exact_n,
+                                            counts, (hipStream_t)stream),
                     fn);
 }
 

@@ -187,13 +187,14 @@ __global__ __launch_bounds__(kThreads) void exact_topk_kernel(Shape sh, const T*
   select_from_keys(sh, unit, nb, topk_idx, topk_score, p);
 }
 
-// Per unit: entries of the exact list in [0, NBmax), how many of them the
-// predicted list holds, and how many are resident by the slot map (-1 without
-// a map).  A bitmap of the predicted blocks lives in LDS; one list entry per
+// Per unit: entries among the first exact_n of the exact list that lie in
+// [0, NBmax), how many of them the predicted list holds, and how many are
+// resident by the slot map (-1 without a map).  A bitmap of the predicted blocks lives in LDS; one list entry per
 // thread (K <= 256).
 __global__ __launch_bounds__(kThreads) void agreement_kernel(Shape sh, const int32_t* __restrict__ pred,
                                                              const int32_t* __restrict__ exact,
                                                              const int32_t* __restrict__ l2p,
+                                                             int exact_n,
                                                              int32_t* __restrict__ counts) {
   __shared__ uint32_t bits[8192 / 32];
   const int unit = blockIdx.x;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void agreement_kernel(Shape sh, const int
     if (j >= 0 && j < sh.NBmax) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
-  int j = t < sh.K ? exact[(size_t)unit * sh.K + t] : -1;
+  int j = t < exact_n ? exact[(size_t)unit * sh.K + t] : -1;
   const bool valid = j >= 0 && j < sh.NBmax;
   const bool agree = valid && ((bits[j >> 5] >> (j & 31)) & 1u);
   const bool res = valid && l2p && l2p[(size_t)unit * sh.NBmax + j] >= 0;
@@ -648,9 +649,9 @@ hipError_t launch_exact_topk(const Shape& sh, int dtype, const void* q, int q_ro
 }
 
 hipError_t launch_agreement(const Shape& sh, const int32_t* pred, const int32_t* exact,
-                            const int32_t* l2p, int32_t* counts, hipStream_t st) {
+                            const int32_t* l2p, int exact_n, int32_t* counts, hipStream_t st) {
   hipLaunchKernelGGL(agreement_kernel, dim3(sh.B * sh.H), dim3(kThreads), 0, st, sh, pred, exact,
-                     l2p, counts);
+                     l2p, exact_n, counts);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ hipError_t launch_exact_topk(const Shape& sh, int dtype, const void* q, int q_ro
                              const void* records, const int32_t* ctx_len, int32_t* topk_idx,
                              float* topk_score, hipStream_t st);
 hipError_t launch_agreement(const Shape& sh, const int32_t* pred, const int32_t* exact,
-                            const int32_t* l2p, int32_t* counts, hipStream_t st);
+                            const int32_t* l2p, int exact_n, int32_t* counts, hipStream_t st);
 hipError_t launch_evict(const Shape& sh, const int32_t* topk_idx, int step, int max_admit,
                         int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
                         int32_t* admit_count, hipStream_t st);

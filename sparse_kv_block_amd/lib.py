@@ -86,7 +86,7 @@ def _load():
         "oasis_dense_attn_workspace_bytes": ([SP], ctypes.c_size_t),
         "oasis_append_token": ([SP, P, P, P, P, P, P, P, P], I32),
         "oasis_exact_topk": ([SP, P, I32, P, P, P, P, P], I32),
-        "oasis_topk_agreement": ([SP, P, P, P, P, P], I32),
+        "oasis_topk_agreement": ([SP, P, P, P, I32, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -211,14 +211,16 @@ def exact_topk(shape: Shape, q, records, ctx_len, topk_idx, topk_score, q_row: i
         _dev(topk_score, "topk_score", torch.float32, U * K), _stream(stream)))
 
 
-def topk_agreement(shape: Shape, pred_idx, exact_idx, counts, l2p=None, stream=None):
-    """Per-unit (n_exact, agreeing, resident) counts (see oasis_topk_agreement)."""
+def topk_agreement(shape: Shape, pred_idx, exact_idx, counts, l2p=None,
+                   exact_n: Optional[int] = None, stream=None):
+    """Per-unit (n_exact, agreeing, resident) counts over the first exact_n
+    entries of the exact list (all K by default; see oasis_topk_agreement)."""
     U, K = shape.units(), shape.k_resident
     lp = None if l2p is None else _dev(l2p, "l2p", I32, U * shape.max_blocks)
     _check(_lib.oasis_topk_agreement(
         ctypes.byref(shape), _dev(pred_idx, "pred_idx", I32, U * K),
-        _dev(exact_idx, "exact_idx", I32, U * K), lp, _dev(counts, "counts", I32, U * 3),
-        _stream(stream)))
+        _dev(exact_idx, "exact_idx", I32, U * K), lp, int(K if exact_n is None else exact_n),
+        _dev(counts, "counts", I32, U * 3), _stream(stream)))
 
 
 def capped_evict(shape: Shape, topk_idx, step: int, max_admit: int, l2p, p2l, last_sel, admit,

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_helpers(L, ora):
     raw = L.raw()
-    assert raw.oasis_abi_version() == 5
+    assert raw.oasis_abi_version() == 6
     for cap, K in [(0.0, 128), (0.01, 128), (0.05, 128), (0.2, 128), (1.0, 128), (0.25, 8),
                    (2.0, 16), (-1.0, 8), (0.3, 10), (0.7, 10)]:
         assert L.cap_to_max_admit(cap, K) == ora.max_admit(cap, K), (cap, K)
@@ -83,8 +83,10 @@ def test_null_pointers_and_bad_scalars(L):
     assert "records is NULL" in L.last_error()
     assert raw.oasis_exact_topk(ctypes.byref(s), p, 2, p, p, p, p, None) == L.ERR_INVALID
     assert "q_row" in L.last_error()
-    assert raw.oasis_topk_agreement(ctypes.byref(s), p, None, p, p, None) == L.ERR_INVALID
+    assert raw.oasis_topk_agreement(ctypes.byref(s), p, None, p, 4, p, None) == L.ERR_INVALID
     assert "exact_idx is NULL" in L.last_error()
+    assert raw.oasis_topk_agreement(ctypes.byref(s), p, p, p, 9, p, None) == L.ERR_INVALID
+    assert "exact_n" in L.last_error()
     assert raw.oasis_score_topk(ctypes.byref(s), p, 2, p, p, p, p, None) == L.ERR_INVALID
     assert raw.oasis_capped_evict(ctypes.byref(s), p, 1, -1, p, p, p, p, p, None) == L.ERR_INVALID
     assert raw.oasis_lookahead_attn(ctypes.byref(s), p, p, p, p, float("nan"), p, None) == L.ERR_INVALID

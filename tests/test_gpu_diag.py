@@ -107,8 +107,9 @@ def test_exact_topk_long_context_and_more_slots_than_blocks():
     check_topk(idx, sc, ref, ex, what="exact long")
 
 
+@pytest.mark.parametrize("exact_n", [None, 1, 7])
 @pytest.mark.parametrize("with_map", [True, False])
-def test_agreement_counts_bit_exact(with_map):
+def test_agreement_counts_bit_exact(with_map, exact_n):
     cfg = small(batch=4, n_kv_heads=3, n_q_heads=6, k_resident=32)
     nbmax = 300
     rng = np.random.default_rng(7)
@@ -126,9 +127,10 @@ def test_agreement_counts_bit_exact(with_map):
     shape = lib.Shape.of(cfg, nbmax)
     counts = torch.full((B, H, 3), 99, dtype=torch.int32, device=DEV)
     lib.topk_agreement(shape, torch.from_numpy(pred).to(DEV), torch.from_numpy(exact).to(DEV),
-                       counts, l2p=torch.from_numpy(l2p).to(DEV) if with_map else None)
+                       counts, l2p=torch.from_numpy(l2p).to(DEV) if with_map else None,
+                       exact_n=exact_n)
     torch.cuda.synchronize()
-    ref = oracle.agreement(pred, exact, l2p if with_map else None)
+    ref = oracle.agreement(pred, exact, l2p if with_map else None, exact_n=exact_n)
     np.testing.assert_array_equal(i32(counts), ref)
 
 
@@ -151,3 +153,49 @@ def test_exact_topk_full_size_qwen3_8b_16k():
         ex = oracle.exact_block_scores(qq, r, c, 16, q_row=1)
         ref, _ = oracle.topk(ex, c, 16, cfg.k_resident)
         check_topk(idx[b:b + 1, h:h + 1], sc[b:b + 1, h:h + 1], ref, ex, what=f"full ({b},{h})")
+
+
+def test_agreement_study_matches_oracle_composition():
+    """Eight look-ahead steps on small-integer inputs (every score exact in
+    fp32, so every list must agree bit for bit): the study's per-unit counts
+    against the same study composed from oracle calls."""
+    from sparse_kv_block_amd.diagnostics import AgreementStudy
+    from sparse_kv_block_amd.pipeline import Layer
+    cfg = small(batch=3, k_resident=12, cap=0.25, n_q_heads=8, n_kv_heads=2)
+    ctx = np.array([1000, 300, 17], np.int32)
+    nbmax = cfg.max_blocks(1000)
+    say("agreement study vs oracle")
+    rec, _ = gen.integer_inputs(cfg, ctx, nbmax, seed=11, device=DEV)
+    qs = gen.integer_queries(cfg, 10, seed=12, device=DEV)
+    m = cfg.max_admit()
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    layer.cold_fill(qs[0], rec)
+    study = AgreementStudy(layer, top=5)
+
+    rec_c = oracle.as_np(rec.cpu())
+    summ_c = oracle.summarize(rec_c, ctx, 16)
+    l2p, p2l, last = (x.cpu().numpy().copy() for x in layer.state())
+    for s in range(1, 9):
+        got = study.step(rec, qs[s], qs[s + 1], s, keep_units=True)
+        q, qn = qs[s].cpu(), qs[s + 1].cpu()
+        _, T, _, _, _ = oracle.layer_step(q, rec_c, summ_c, ctx, 16, cfg.k_resident, s, m,
+                                          l2p, p2l, last)
+        E, _ = oracle.topk(oracle.exact_block_scores(qn, rec_c, ctx, 16, 0), ctx, 16,
+                           cfg.k_resident)
+        lists = {
+            "pred": (T, l2p),
+            "bound": (oracle.topk(oracle.block_scores(qn, summ_c, ctx, 16, 0), ctx, 16,
+                                  cfg.k_resident)[0], None),
+            "drift": (oracle.topk(oracle.exact_block_scores(q, rec_c, ctx, 16, 1), ctx, 16,
+                                  cfg.k_resident)[0], None),
+            "previous": (oracle.topk(oracle.block_scores(q, summ_c, ctx, 16, 0), ctx, 16,
+                                     cfg.k_resident)[0], None),
+        }
+        for name, (P, lp) in lists.items():
+            np.testing.assert_array_equal(got[name], oracle.agreement(P, E, lp),
+                                          err_msg=f"step {s} {name}")
+            np.testing.assert_array_equal(got[name + "@top"], oracle.agreement(P, E, lp, 5),
+                                          err_msg=f"step {s} {name} top 5")
+        assert got["resident"] is got["pred"]
+        np.testing.assert_array_equal(i32(layer.l2p), l2p)

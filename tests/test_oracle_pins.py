@@ -500,3 +500,5 @@ def test_agreement_counts(ora):
     l2p[0, 0, [3, 5, 7]] = [0, 1, 2]
     assert ora.agreement(pred, exact, l2p)[0, 0].tolist() == [3, 2, 2]
     assert ora.agreement(exact, exact)[0, 0].tolist() == [3, 3, -1]
+    # recall of the exact list's two best blocks: 2 and 3; only 2 is predicted
+    assert ora.agreement(pred, exact, l2p, exact_n=2)[0, 0].tolist() == [2, 1, 1]
