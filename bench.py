@@ -205,6 +205,92 @@ def agreement_leg(cfg, ctx, nbmax, steps: int, caps, sigmas):
     return out
 
 
+def capmodel_leg(cfg, layer, rec_host, ctx, nbmax, qs, t_layer_s: float, gather: dict,
+                 pipeline: dict = None, layers: int = 36, caps=(0.01, 0.05, 0.2, 1.0)):
+    """Host-link budget (sparse_kv_block_amd.capmodel): measured link rates
+    (the gather kernel's, and one large SDMA copy from the pinned pool),
+    measured fused-step times at K and at the smaller K/2, the largest cap
+    whose bytes hide in a `layers`-layer decode step, and the predicted step
+    times beside the measured 36-layer pipeline when it ran."""
+    import torch
+    from sparse_kv_block_amd import capmodel as cm
+    from sparse_kv_block_amd import lib
+    from sparse_kv_block_amd.pipeline import Layer
+    dev = layer.device
+    stream = torch.cuda.current_stream()
+    # SDMA: one contiguous 1 GiB host-to-device copy from the pinned pool
+    flat = rec_host.view(-1)
+    n = min(flat.numel(), (1 << 30) // flat.element_size())
+    dst = torch.empty(n, dtype=flat.dtype, device=dev)
+    dst.copy_(flat[:n], non_blocking=True)
+    ts = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(flat[:n], non_blocking=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    sdma_Bps = n * flat.element_size() / float(np.median(ts))
+    del dst
+    # the smaller-K variant: the fused step at K/2
+    K2 = cfg.k_resident // 2
+    c2 = cfg.scaled(k_resident=K2)
+    l2 = Layer(c2, ctx, nbmax, device=dev)
+    l2.summ.copy_(layer.summ)
+    l2.cold_fill(qs[0], rec_host)
+    for i in range(5):
+        l2.step(qs[i % len(qs)], i + 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(20)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        l2.step(qs[i % len(qs)], i + 6)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_half_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    del l2
+    torch.cuda.empty_cache()
+
+    units = cfg.batch * cfg.n_kv_heads
+    rec_bytes = lib.record_bytes(layer.shape)
+    gather_Bps = gather["bytes"] / gather["device_s"]
+    out = {"layers": layers, "units": units, "record_bytes": rec_bytes,
+           "link_GBps": {"gather_kernel": round(gather_Bps / 1e9, 2),
+                         "sdma_1GiB_copy": round(sdma_Bps / 1e9, 2)},
+           "fused_step_us": {str(cfg.k_resident): round(t_layer_s * 1e6, 1),
+                             str(K2): round(t_half_s * 1e6, 1)},
+           "largest_hidden": [], "predicted_step_ms": []}
+    for K, t in ((cfg.k_resident, t_layer_s), (K2, t_half_s)):
+        window = layers * t
+        for name, bw in (("gather_kernel", gather_Bps), ("sdma_1GiB_copy", sdma_Bps)):
+            m = cm.largest_hidden_admit(bw, window, layers, units, rec_bytes, K)
+            out["largest_hidden"].append({"K": K, "link": name, "window_ms": round(window * 1e3, 3),
+                                          "max_admit": m, "cap": round(m / K, 5),
+                                          "bytes": cm.bytes_per_step(layers, units, m, rec_bytes)})
+    window = layers * t_layer_s
+    measured, moved = {}, {}
+    if pipeline:
+        measured = {row["cap"]: row["step_ms"] for row in pipeline["caps"]}
+        moved = {row["cap"]: row["bytes_per_step"] for row in pipeline["caps"]}
+    for cap in caps:
+        m = cfg.max_admit(cap)
+        nbytes = cm.bytes_per_step(layers, units, m, rec_bytes)
+        out["predicted_step_ms"].append({
+            "cap": cap, "max_admit": m, "bytes": nbytes,
+            "overlapped_ms": round(cm.predicted_step_s(window, nbytes, gather_Bps) * 1e3, 2),
+            "serial_ms": round(cm.predicted_step_s(window, nbytes, gather_Bps, False) * 1e3, 2),
+            "measured_ms": measured.get(cap),
+            # the bound assumes every unit finds m misses; with the bytes the
+            # pipeline actually moved:
+            "overlapped_ms_moved_bytes": (round(cm.predicted_step_s(window, moved[cap], gather_Bps)
+                                                * 1e3, 2) if cap in moved else None)})
+    log(f"[bench] cap model: link gather {gather_Bps / 1e9:.1f} GB/s, SDMA {sdma_Bps / 1e9:.1f} GB/s; "
+        f"fused step K={cfg.k_resident} {t_layer_s * 1e6:.0f} us, K={K2} {t_half_s * 1e6:.0f} us; "
+        f"hidden: {[(h['K'], h['link'], h['max_admit']) for h in out['largest_hidden']]}")
+    return out
+
+
 def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
     """The 36-layer decode step with the fetch-cap sweep: per layer the fused
     step on the main stream and the gather prefetch of its admissions on a side
@@ -297,6 +383,9 @@ def main():
                     help="also time the dense comparator (attention over the full HBM-resident KV)")
     ap.add_argument("--append", action="store_true",
                     help="also time the decode append (after every other GPU leg)")
+    ap.add_argument("--capmodel", action="store_true",
+                    help="also measure the host-link budget (SDMA copy, K/2 step) and the "
+                         "largest cap that hides in a 36-layer step")
     ap.add_argument("--agreement", action="store_true",
                     help="also run the top-K agreement study (after every other GPU leg; "
                          "releases the timed layer's buffers)")
@@ -437,6 +526,13 @@ def main():
     if args.pipeline:
         result["pipeline_36_layer"] = pipeline_leg(layer, rec_host, args.pipeline_steps, 2)
 
+    if args.capmodel:
+        if "pcie" not in result:
+            log("[bench] --capmodel needs the prefetch leg (drop --no-pcie)")
+        else:
+            result["cap_model"] = capmodel_leg(cfg, layer, rec_host, ctx, nbmax, qs, avg_kernel_s,
+                                               result["pcie"]["gather"],
+                                               result.get("pipeline_36_layer"))
     if args.append:
         result["append"] = append_leg(layer, rec_host)
     if args.agreement:
