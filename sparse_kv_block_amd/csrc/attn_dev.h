@@ -92,17 +92,22 @@ struct AttnWave {
     unit_pool = unit_base;
   }
 
-  // This wave's slot range.
-  __device__ __forceinline__ int slot_begin(const Shape& sh) const { return (sh.K * split) / NSPLIT; }
-  __device__ __forceinline__ int slot_end(const Shape& sh) const { return (sh.K * (split + 1)) / NSPLIT; }
+  // This wave's slots are split, split + NSPLIT, split + 2*NSPLIT, ...: the
+  // waves of a workgroup take consecutive records in turn, so at any moment
+  // they stream one contiguous region of the pool rather than NSPLIT separate
+  // ones (measured ~5% more HBM bandwidth on gfx950).
+  __device__ __forceinline__ int n_slots(const Shape& sh) const {
+    return split < sh.K ? (sh.K - split + NSPLIT - 1) / NSPLIT : 0;
+  }
+  __device__ __forceinline__ int slot_of(int i) const { return split + NSPLIT * i; }
 
-  // Valid-token count of slot cb + lane (lanes past the range give 0).
+  // Valid-token count of this wave's slot number ib + lane (lanes past ie give 0).
   __device__ __forceinline__ int slot_tokens(const Shape& sh, const int32_t* __restrict__ p2l, int unit,
-                                             int L, int cb, int ce) const {
+                                             int L, int ib, int ie) const {
     const int lane = threadIdx.x % kWave;
     int nv_l = 0;
-    if (lane < ce - cb) {
-      const int j = p2l[(size_t)unit * sh.K + cb + lane];
+    if (lane < ie - ib) {
+      const int j = p2l[(size_t)unit * sh.K + slot_of(ib + lane)];
       if (j >= 0 && j < sh.NBmax) {
         const int nv = L - j * kBlock;
         nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
@@ -259,9 +264,9 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
   a.init(sh, q, pool + (size_t)unit * sh.K * AW::REC, b, h);
   // This wave's slots, 64 at a time; within a group two register buffers
   // alternate: while one block is processed the next one's loads are in flight.
-  const int s0 = a.slot_begin(sh), s1 = a.slot_end(sh);
-  for (int cb = s0; cb < s1; cb += kWave) {
-    const int nv_l = a.slot_tokens(sh, p2l, unit, L, cb, s1);
+  const int ns = a.n_slots(sh);
+  for (int cb = 0; cb < ns; cb += kWave) {
+    const int nv_l = a.slot_tokens(sh, p2l, unit, L, cb, ns);
     uint64_t todo = ballot(nv_l > 0);
     auto pop = [&]() -> int {
       if (!todo) return -1;
@@ -272,14 +277,14 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
     bf16x8 ka[AW::KS], kb[AW::KS];
     i16x4 va[AW::NT], vb[AW::NT];
     int sa = pop();
-    if (sa >= 0) a.load(cb + sa, ka, va);
+    if (sa >= 0) a.load(a.slot_of(cb + sa), ka, va);
     while (sa >= 0) {
       const int sb = pop();
-      if (sb >= 0) a.load(cb + sb, kb, vb);
+      if (sb >= 0) a.load(a.slot_of(cb + sb), kb, vb);
       a.process(ka, va, __builtin_amdgcn_readlane(nv_l, sa), scale_log2);
       if (sb < 0) break;
       sa = pop();
-      if (sa >= 0) a.load(cb + sa, ka, va);
+      if (sa >= 0) a.load(a.slot_of(cb + sa), ka, va);
       a.process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb), scale_log2);
     }
   }

@@ -3,8 +3,9 @@
 // Every per-unit kernel runs one 256-thread workgroup per (request, KV head):
 // the units are independent (their blocks, summaries, maps and slots are
 // disjoint), so nothing crosses workgroups and the launch needs no inter-block
-// synchronisation.  At batch 128 x 8 KV heads that is 1024 workgroups, four
-// per CU on the 256 CUs, all resident at once.
+// synchronisation.  At batch 128 x 8 KV heads that is 1024 workgroups; the
+// fused step's register use (about 220 VGPRs, two waves per SIMD) places two
+// per CU, so they run in two even rounds over the 256 CUs.
 #include "attn_dev.h"
 #include "diag_dev.h"
 #include "launch.h"
@@ -506,11 +507,13 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(Shape sh, const
   }
   AW a;
   a.init(sh, q, rec + (size_t)unit * sh.NBmax * AW::REC, b, h);
+  // wave w takes blocks j0 + w, j0 + w + 4, ...: the four waves stream one
+  // contiguous region together
   const int lane = threadIdx.x % kWave;
-  const int jw = j0 + a.w * (kDenseChunk / kWaves);
+  auto blk = [&](int i) { return j0 + a.w + kWaves * i; };
   int nv_l = 0;
-  if (lane < kDenseChunk / kWaves && jw + lane < nb) {
-    const int nv = L - (jw + lane) * kBlock;
+  if (lane < kDenseChunk / kWaves && blk(lane) < nb) {
+    const int nv = L - blk(lane) * kBlock;
     nv_l = nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
   }
   uint64_t todo = ballot(nv_l > 0);
@@ -523,14 +526,14 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(Shape sh, const
   bf16x8 ka[AW::KS], kb[AW::KS];
   i16x4 va[AW::NT], vb[AW::NT];
   int sa = pop();
-  if (sa >= 0) a.load(jw + sa, ka, va);
+  if (sa >= 0) a.load(blk(sa), ka, va);
   while (sa >= 0) {
     const int sb = pop();
-    if (sb >= 0) a.load(jw + sb, kb, vb);
+    if (sb >= 0) a.load(blk(sb), kb, vb);
     a.process(ka, va, __builtin_amdgcn_readlane(nv_l, sa), scale_log2);
     if (sb < 0) break;
     sa = pop();
-    if (sa >= 0) a.load(jw + sa, ka, va);
+    if (sa >= 0) a.load(blk(sa), ka, va);
     a.process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb), scale_log2);
   }
   a.merge_store(sh, b, h, nullptr, reinterpret_cast<float*>(smem), mypart);

@@ -16,9 +16,8 @@
 
 namespace oasis {
 
-// Requires this wave's slot range to be at most 64 slots (K <= 256 with one
-// row tile, K <= 128 with two).  Writes keys[j] for j < nb and the attention
-// output; ends with the attention merge (so the keys are complete in LDS for
+// Requires at most 64 slots per wave (K <= 256 with one row tile, K <= 128
+// with two).  Writes keys[j] for j < nb and the attention output; ends with the attention merge (so the keys are complete in LDS for
 // the whole workgroup afterwards).
 template <int D, int RT, int SG, int UL, int TW = RT>
 __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
@@ -72,8 +71,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   };
 
   // ---- interleaved steps: one block + SG record groups each ----
-  const int s0 = a.slot_begin(sh), s1 = a.slot_end(sh);
-  const int nv_l = a.slot_tokens(sh, p2l, unit, L, s0, s1);
+  const int nv_l = a.slot_tokens(sh, p2l, unit, L, 0, a.n_slots(sh));
   uint64_t todo = ballot(nv_l > 0);
   auto pop = [&]() -> int {
     if (!todo) return -1;
@@ -87,13 +85,13 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   int steps = 0;
   int sa = pop();
   if (sa >= 0) {
-    a.load(s0 + sa, ka, va);
+    a.load(a.slot_of(sa), ka, va);
     load_groups(0, SG, la, ha);
   }
   while (sa >= 0) {
     const int sb = pop();
     if (sb >= 0) {
-      a.load(s0 + sb, kb, vb);
+      a.load(a.slot_of(sb), kb, vb);
       load_groups(SG * (steps + 1), SG, lb, hb);
     }
     a.process(ka, va, __builtin_amdgcn_readlane(nv_l, sa), scale_log2);
@@ -102,7 +100,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
     if (sb < 0) break;
     sa = pop();
     if (sa >= 0) {
-      a.load(s0 + sa, ka, va);
+      a.load(a.slot_of(sa), ka, va);
       load_groups(SG * (steps + 1), SG, la, ha);
     }
     a.process(kb, vb, __builtin_amdgcn_readlane(nv_l, sb), scale_log2);
