@@ -128,7 +128,8 @@ __device__ __forceinline__ SelectPtrs select_ptrs(char* smem, int NBmax, int K) 
 __device__ __forceinline__ void select_from_keys(const Shape& sh, int unit, int nb,
                                                  int32_t* topk_idx, float* topk_score,
                                                  const SelectPtrs& p) {
-  const int kk = topk_unit(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  const int kk = topk_unit<kMaxKpt>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                     p.cand_key, p.ev.red);
   for (int t = threadIdx.x; t < sh.K; t += kThreads) {
     if (t >= kk) p.sel_idx[t] = -1;
     topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
@@ -400,7 +401,8 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   auto scan_select = [&]() -> int {
     scan_unit<T, D, U>(sh, q, 1, summ + ((size_t)unit * sh.NBmax + c0) * 2 * D, b, h, len, p.keys);
     __syncthreads();
-    return topk_unit(p.keys, len, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+    return topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                            p.cand_key, p.ev.red);
   };
   int kk = 0;
   if (!whole) {
@@ -413,7 +415,8 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
           sh, q, pool, p2l, summ + (size_t)unit * sh.NBmax * 2 * D, nb, b, h, L, scale, out,
           reinterpret_cast<float*>(smem), p.keys);
       __syncthreads();
-      kk = topk_unit(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+      kk = topk_unit<kScanChunk / kThreads>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                            p.cand_key, p.ev.red);
     }
   } else if (scan_first(unit)) {
     kk = scan_select();
@@ -456,7 +459,8 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
       total += n;
     }
     __syncthreads();
-    kk = topk_unit(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+    kk = topk_unit<kScanChunk / kThreads>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                          p.cand_key, p.ev.red);
     for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
     if (tid == 0) ws.counter[unit] = 0;    // ready for the next launch
   } else {

@@ -138,82 +138,130 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
 }
 
 // ---------------------------------------------------------------- top-K
-// Scratch `red` (LDS ints): [2][kWaves][4] counts + one shared counter.
-constexpr int kRedInts = 2 * kWaves * 4 + 4;
+// Most keys one top-K call handles per thread (kMaxKpt * 256 = 8192 blocks).
+constexpr int kMaxKpt = 32;
+// Scratch `red` (LDS ints): [2][kWaves][4] counts (eviction), four spare
+// ints (the fused step keeps a flag in the second), [2][kMaxKpt][kWaves]
+// compaction counts, then three 256-bin radix histograms.
+constexpr int kRedHist = 2 * kWaves * 4 + 4 + 2 * kMaxKpt * kWaves;
+constexpr int kRedInts = kRedHist + 3 * 256;
 
 // Selects the min(K, nb) best keys; writes sel_idx[0..kk) / sel_key[0..kk) in
-// (key desc, index asc) order and returns kk.  cand_* are K-entry scratch.
+// (key desc, index asc) order and returns kk.  cand_* are (K + 4)-entry
+// scratch.  Requires nb <= KPT * kThreads.  Thread t holds keys t, t + 256,
+// ... in registers for the whole selection.
+template <int KPT>
 __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, int* sel_idx,
                                          uint32_t* sel_key, int* cand_idx, uint32_t* cand_key,
                                          int* red) {
+  static_assert(KPT >= 1 && KPT <= kMaxKpt, "keys per thread");
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int kk = K < nb ? K : nb;
   if (kk <= 0) return 0;
-  // 1. K-th largest key T = max{v : #{key >= v} >= kk}, two bits per round:
-  //    the three candidates of the next two bits are counted with ballots.
-  uint32_t T = 0;
-  int parity = 0;
-  for (int shift = 30; shift >= 0; shift -= 2) {
-    const uint32_t c1 = T | (1u << shift), c2 = T | (2u << shift), c3 = T | (3u << shift);
-    int n1 = 0, n2 = 0, n3 = 0;
-    for (int base = 0; base < nb; base += kThreads) {
-      const int j = base + tid;
-      const uint32_t k = j < nb ? keys[j] : 0u;
-      n1 += __popcll(ballot(k >= c1));
-      n2 += __popcll(ballot(k >= c2));
-      n3 += __popcll(ballot(k >= c3));
-    }
-    int* r = red + (parity * kWaves + w) * 4;
-    if (lane_id() == 0) { r[0] = n1; r[1] = n2; r[2] = n3; }
-    __syncthreads();
-    int t1 = 0, t2 = 0, t3 = 0;
+  const int act = (nb + kThreads - 1) / kThreads;   // chunks holding keys (uniform)
+  uint32_t k[KPT];
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const int* rv = red + (parity * kWaves + v) * 4;
-      t1 += rv[0];
-      t2 += rv[1];
-      t3 += rv[2];
-    }
-    T = t3 >= kk ? c3 : (t2 >= kk ? c2 : (t1 >= kk ? c1 : T));
-    parity ^= 1;
+  for (int i = 0; i < KPT; ++i) {
+    const int j = i * kThreads + tid;
+    k[i] = (i < act && j < nb) ? keys[j] : 0u;
   }
-  // 2. compact: keys > T anywhere, then the lowest-index keys == T.
-  int* cnt_gt = red + 2 * kWaves * 4;
-  if (tid == 0) *cnt_gt = 0;
+  // 1. K-th largest key T = max{v : #{key >= v} >= kk} by radix selection,
+  //    eight bits per round from the top: the keys that match the digits
+  //    chosen so far are counted per next digit in an LDS histogram (one
+  //    barrier per round); then every wave finds, on its own, the digit at
+  //    which the count of larger keys reaches kk.  Three histograms rotate
+  //    so that clearing one never races with the use of another.  Key 0 is
+  //    never a score key (score_key maps every finite score above it) and
+  //    marks the padding.
+  int* hist = red + kRedHist;
+  const int lane = lane_id();
+  hist[tid] = 0;
+  hist[kThreads + tid] = 0;
   __syncthreads();
-  for (int base = 0; base < nb; base += kThreads) {
-    const int j = base + tid;
-    if (j < nb && keys[j] > T) {
-      const int p = atomicAdd(cnt_gt, 1);
-      cand_idx[p] = j;
-      cand_key[p] = keys[j];
+  uint32_t T = 0, mask = 0;
+  int rem = kk;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int shift = 24 - 8 * r;
+    int* hb = hist + (r % 3) * 256;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (i < act && k[i] != 0u && (k[i] & mask) == T) atomicAdd(&hb[(k[i] >> shift) & 255u], 1);
+    __syncthreads();
+    // lane l holds digits 255-4l .. 252-4l (descending); inclusive prefix of
+    // their counts over the lanes
+    const int4 c4 = *reinterpret_cast<const int4*>(hb + 252 - 4 * lane);
+    const int c[4] = {c4.w, c4.z, c4.y, c4.x};            // digits 255-4l, 254-4l, ...
+    const int sum = c[0] + c[1] + c[2] + c[3];
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      incl += lane >= o ? v : 0;
+    }
+    const int excl = incl - sum;
+    const uint64_t cross = ballot(excl < rem && incl >= rem);
+    const int L = __builtin_ctzll(cross);
+    int above = excl, q = 0;
+    bool found = false;
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      found = found || above + c[e] >= rem;
+      if (!found) { above += c[e]; q = e + 1; }
+    }
+    const int digit = __shfl(255 - 4 * lane - q, L);
+    rem -= __shfl(above, L);
+    T |= (uint32_t)digit << shift;
+    mask |= 255u << shift;
+    hist[((r + 2) % 3) * 256 + tid] = 0;                    // for round r + 2
+  }
+  // 2. compact in index order (chunk, wave, lane): every key > T, then the
+  //    lowest-index keys == T up to kk.  One barrier: each wave publishes its
+  //    per-chunk counts, every thread then sums the counts before its own.
+  int* cg = red + 2 * kWaves * 4 + 4;
+  int* ce = cg + kMaxKpt * kWaves;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (i < act) {
+      const int g = __popcll(ballot(k[i] > T));
+      const int e = __popcll(ballot(k[i] == T));
+      if (lane_id() == 0) { cg[i * kWaves + w] = g; ce[i * kWaves + w] = e; }
     }
   }
   __syncthreads();
-  const int ngt = *cnt_gt;
+  int ngt = 0;
+  for (int x = 0; x < act * kWaves; ++x) ngt += cg[x];
   const int need = kk - ngt;
-  int taken = 0;
-  for (int base = 0; base < nb && taken < need; base += kThreads) {
-    const int j = base + tid;
-    const bool eq = j < nb && keys[j] == T;
-    const uint64_t m = ballot(eq);
-    if (lane_id() == 0) red[(parity * kWaves + w) * 4] = __popcll(m);
-    __syncthreads();
-    int off = 0, tot = 0;
+  int run_g = 0, run_e = 0;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const int c = red[(parity * kWaves + v) * 4];
-      off += v < w ? c : 0;
-      tot += c;
+  for (int i = 0; i < KPT; ++i) {
+    if (i < act) {
+      int og = run_g, oe = run_e;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const int g = cg[i * kWaves + v], e = ce[i * kWaves + v];
+        og += v < w ? g : 0;
+        oe += v < w ? e : 0;
+        run_g += g;
+        run_e += e;
+      }
+      const bool gt = k[i] > T, eq = k[i] == T;
+      const uint64_t mg = ballot(gt), me = ballot(eq);
+      const int j = i * kThreads + tid;
+      if (gt) {
+        const int pos = og + lanes_below(mg);
+        cand_idx[pos] = j;
+        cand_key[pos] = k[i];
+      }
+      if (eq) {
+        const int r = oe + lanes_below(me);
+        if (r < need) {
+          cand_idx[ngt + r] = j;
+          cand_key[ngt + r] = T;
+        }
+      }
     }
-    const int r = taken + off + lanes_below(m);
-    if (eq && r < need) {
-      cand_idx[ngt + r] = j;
-      cand_key[ngt + r] = T;
-    }
-    taken += tot;
-    parity ^= 1;
   }
   // pad to a multiple of 4 so the ranking can read four entries at a time
   if (tid < ((kk + 3) & ~3) - kk) {
@@ -221,21 +269,44 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     cand_idx[kk + tid] = 0x7FFFFFFF;
   }
   __syncthreads();
-  // 3. rank the kk candidates by (key desc, index asc).
-  if (tid < kk) {
-    const uint32_t k = cand_key[tid];
-    const int j = cand_idx[tid];
+  // 3. rank the kk candidates by (key desc, index asc).  Up to 128
+  //    candidates: two threads per candidate, each over half of the list.
+  const int kk4 = (kk + 3) >> 2;
+  auto rank_range = [&](uint32_t key, int j, int p0, int p1) {
     int rank = 0;
-    const int kk4 = (kk + 3) >> 2;
 #pragma unroll 4
-    for (int p = 0; p < kk4; ++p) {
+    for (int p = p0; p < p1; ++p) {
       const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
       const u32x4 jp = reinterpret_cast<const u32x4*>(cand_idx)[p];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rank += (kp[e] > k) || (kp[e] == k && (int)jp[e] < j);
+      for (int e = 0; e < 4; ++e) rank += (kp[e] > key) || (kp[e] == key && (int)jp[e] < j);
     }
+    return rank;
+  };
+  if (kk <= kThreads / 2) {
+    const int c = tid % (kThreads / 2), half = tid / (kThreads / 2);
+    const int h4 = (kk4 + 1) >> 1;
+    int rank = 0;
+    uint32_t key = 0;
+    int j = 0;
+    if (c < kk) {
+      key = cand_key[c];
+      j = cand_idx[c];
+      rank = half ? rank_range(key, j, h4, kk4) : rank_range(key, j, 0, h4);
+    }
+    if (half && c < kk) cg[c] = rank;                 // compaction counts are spent
+    __syncthreads();
+    if (!half && c < kk) {
+      rank += cg[c];
+      sel_idx[rank] = j;
+      sel_key[rank] = key;
+    }
+  } else if (tid < kk) {
+    const uint32_t key = cand_key[tid];
+    const int j = cand_idx[tid];
+    const int rank = rank_range(key, j, 0, kk4);
     sel_idx[rank] = j;
-    sel_key[rank] = k;
+    sel_key[rank] = key;
   }
   __syncthreads();
   return kk;
