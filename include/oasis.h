@@ -247,20 +247,20 @@ oasis_status oasis_topk_agreement(const oasis_shape* shape,
 
 /* Workspace bytes oasis_layer_step needs for a shape: 0 while
  * max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K lists
- * of the split summary scan and one counter per unit). */
+ * of the split summary scan). */
 size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape);
 
 /* S1..S4 fused — one look-ahead layer step in one launch: attention of both
  * rows over the current resident set (written to out), then the draft row's
  * summary scan, top-K and capped eviction as above.  Results are identical to
  * oasis_lookahead_attn, oasis_score_topk(q_row = 1) and oasis_capped_evict
- * called in that order on one stream.  Contexts longer than 1024 blocks split
- * the scan of a unit over several workgroups that meet in `workspace`
- * (device memory, 256-byte aligned, at least
+ * called in that order on one stream.  When max_blocks exceeds 1024 the scan
+ * of a long context is split over several workgroups whose partial top-K
+ * lists go to `workspace` (device memory, 256-byte aligned, at least
  * oasis_layer_step_workspace_bytes(shape) bytes; NULL allowed when that is
- * 0).  The caller zero-fills the workspace once before its first use; every
- * call leaves it ready for the next.  Calls that may run concurrently need
- * separate workspaces. */
+ * 0), and a second launch merges them and runs the eviction.  The workspace
+ * needs no initialisation; calls that may run concurrently need separate
+ * workspaces. */
 oasis_status oasis_layer_step(const oasis_shape* shape, const void* q,
                               const void* pool, const void* summ,
                               const int32_t* ctx_len, float scale,

@@ -98,11 +98,10 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 }
 
 // ---- split summary scan of long contexts (fused layer step) ----
-constexpr int kScanChunk = 2048;   // blocks per scan part
+constexpr int kScanChunk = 1024;   // blocks per scan part
 
 struct StepWorkspace {
-  int32_t* counter;   // [units]         parts finished (reset to 0 by the last one)
-  int32_t* n;         // [units][parts]  length of each part's list
+  int32_t* n;         // [units][parts]  length of each scan part's list
   uint32_t* key;      // [units][parts][K]
   int32_t* idx;       // [units][parts][K]
 };
@@ -120,16 +119,13 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 
 __host__ __device__ inline size_t step_workspace_bytes(int units, int parts, int K) {
   if (parts <= 1) return 0;
-  return align256((size_t)units * 4) + align256((size_t)units * parts * 4) +
-         2 * align256((size_t)units * parts * K * 4);
+  return align256((size_t)units * parts * 4) + 2 * align256((size_t)units * parts * K * 4);
 }
 
 __host__ __device__ inline StepWorkspace step_workspace(void* base, int units, int parts, int K) {
-  StepWorkspace w{nullptr, nullptr, nullptr, nullptr};
+  StepWorkspace w{nullptr, nullptr, nullptr};
   if (parts <= 1 || base == nullptr) return w;
   char* p = static_cast<char*>(base);
-  w.counter = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)units * 4);
   w.n = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)units * parts * 4);
   w.key = reinterpret_cast<uint32_t*>(p);

@@ -360,14 +360,13 @@ __host__ __device__ constexpr int attn_region(int D, int RT) {
 
 // Long contexts (more than kScanChunk blocks) split a unit over several
 // workgroups: part 0 runs the attention, part p >= 1 scans blocks
-// [(p-1)*kScanChunk, p*kScanChunk) and selects its local top-K.  Each part
-// publishes its list (the attention part an empty one) to the workspace; the
-// part that finishes last (device-scope counter) concatenates the lists in part
-// order and selects the final top-K from them, then runs the eviction, which
-// therefore follows the unit's attention.  The concatenation keeps equal keys
-// in ascending block order (each list is sorted by (key desc, block asc) and
-// the parts cover ascending block ranges), so the result is the same as one
-// workgroup scanning the whole context.
+// [(p-1)*kScanChunk, p*kScanChunk), selects its local top-K and publishes it
+// to the workspace.  A second kernel (split_select_kernel) then concatenates
+// the lists of each split unit, selects its final top-K and runs the
+// eviction; the kernel boundary orders it after the unit's attention and
+// makes the lists visible, with no device-scope fence per workgroup (on
+// gfx950 such a fence writes back or invalidates an XCD's whole L2, which
+// cost more than the scan itself).
 template <typename T, int D, int RT, int U, bool IL>
 __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     Shape sh, const T* __restrict__ q, const T* __restrict__ pool, const T* __restrict__ summ,
@@ -427,45 +426,61 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   }
 
   if (!whole) {
+    if (part == 0) return;                 // attention only
     const size_t slot = (size_t)unit * parts + part;
     for (int t = tid; t < sh.K; t += kThreads) {
       ws.key[slot * sh.K + t] = t < kk ? p.sel_key[t] : 0u;
       ws.idx[slot * sh.K + t] = t < kk ? c0 + p.sel_idx[t] : -1;
     }
     if (tid == 0) ws.n[slot] = kk;
-    // Release: after the barrier every wave's stores are issued; one
-    // device-scope fence (an L2 write-back on gfx950, one per workgroup rather
-    // than one per wave) publishes them before the counter increment.
-    __syncthreads();
-    int* flag = p.ev.red + 2 * kWaves * 4 + 1;
-    if (tid == 0) {
-      __threadfence();
-      *flag = atomicAdd(ws.counter + unit, 1) == active - 1;
-      if (*flag) __threadfence();          // acquire the other parts' lists
-    }
-    __syncthreads();
-    if (!*flag) return;                    // another part finishes the unit
-    uint32_t* mkey = reinterpret_cast<uint32_t*>(smem + attn_bytes +
-                                                 SelectLds(sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk, sh.K).total);
-    int* midx = reinterpret_cast<int*>(mkey + parts * sh.K);
-    int total = 0;
-    for (int pp = 0; pp < active; ++pp) {
-      const size_t sl = (size_t)unit * parts + pp;
-      const int n = ws.n[sl];
-      for (int r = tid; r < n; r += kThreads) {
-        mkey[total + r] = ws.key[sl * sh.K + r];
-        midx[total + r] = ws.idx[sl * sh.K + r];
-      }
-      total += n;
-    }
-    __syncthreads();
-    kk = topk_unit<kScanChunk / kThreads>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                          p.cand_key, p.ev.red);
-    for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
-    if (tid == 0) ws.counter[unit] = 0;    // ready for the next launch
-  } else {
-    for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] += c0;
+    return;                                // split_select_kernel finishes the unit
   }
+  __syncthreads();
+  for (int t = tid; t < sh.K; t += kThreads) {
+    if (t >= kk) p.sel_idx[t] = -1;
+    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
+    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
+  }
+  __syncthreads();
+  evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
+             p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
+             admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+}
+
+// Second kernel of a split step: for every unit whose context exceeds
+// kScanChunk blocks, the scan parts' lists (each sorted by (key desc, block
+// asc), covering ascending block ranges) are concatenated in part order, so
+// equal keys stay in ascending block order and the final top-K equals that of
+// one scan over the whole context; then the capped eviction.
+__global__ __launch_bounds__(kThreads) void split_select_kernel(
+    Shape sh, const int32_t* __restrict__ ctx, int step, int max_admit,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l,
+    int32_t* last_sel, int32_t* admit, int32_t* admit_count, int parts, StepWorkspace ws) {
+  extern __shared__ __align__(16) char smem[];
+  const int unit = blockIdx.x;
+  const int nb = n_blocks(ctx[unit / sh.H], sh.NBmax);
+  if (nb <= kScanChunk) return;            // finished by the step kernel
+  const int active = 1 + scan_parts(nb);
+  const int tid = threadIdx.x;
+  const SelectPtrs p = select_ptrs(smem, 0, sh.K);
+  uint32_t* mkey = reinterpret_cast<uint32_t*>(smem + SelectLds(0, sh.K).total);
+  int* midx = reinterpret_cast<int*>(mkey + parts * sh.K);
+  int total = 0;
+  for (int pp = 1; pp < active; ++pp) {
+    const size_t sl = (size_t)unit * parts + pp;
+    int n = ws.n[sl];
+    n = n < 0 ? 0 : (n > sh.K ? sh.K : n);
+    for (int r = tid; r < n; r += kThreads) {
+      mkey[total + r] = ws.key[sl * sh.K + r];
+      midx[total + r] = ws.idx[sl * sh.K + r];
+    }
+    total += n;
+  }
+  __syncthreads();
+  // up to (8192 / kScanChunk) lists of K <= 256 entries: at most 8192 keys
+  const int kk = topk_unit<kMaxKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                    p.cand_key, p.ev.red);
+  for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
   __syncthreads();
   for (int t = tid; t < sh.K; t += kThreads) {
     if (t >= kk) p.sel_idx[t] = -1;
@@ -711,10 +726,9 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
   const StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
   dim3 grid(sh.B * sh.H * parts);
   const size_t sel = SelectLds(sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk, sh.K).total;
-  const size_t merge = parts > 1 ? (size_t)parts * sh.K * 8 : 0;
   if (dtype == 1) {
     const int rt = rt_of(sh.G);
-    const size_t lds = attn_region(sh.d, rt) + sel + merge;
+    const size_t lds = attn_region(sh.d, rt) + sel;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
     const float sl = sc * kLog2e;
     // One scan part per unit: attention and scan interleaved in one pass (at
@@ -737,7 +751,7 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     }
 #undef OASIS_STEP
   } else {
-    const size_t lds = sel + merge;
+    const size_t lds = sel;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
 #define OASIS_STEP32(D_)                                                                        \
   hipLaunchKernelGGL((layer_step_kernel<float, D_, 1, 4, false>), grid, dim3(kThreads), lds, st, sh,    \
@@ -746,6 +760,15 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
                      admit_count, parts, ws)
     if (sh.d == 128) OASIS_STEP32(128); else OASIS_STEP32(64);
 #undef OASIS_STEP32
+  }
+  if (parts > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = SelectLds(0, sh.K).total + (size_t)parts * sh.K * 8;
+    if (lds > kMaxLds) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(split_select_kernel, dim3(sh.B * sh.H), dim3(kThreads), lds, st, sh, ctx,
+                       step, max_admit, topk_idx, topk_score, l2p, p2l, last_sel, admit,
+                       admit_count, parts, ws);
   }
   return hipGetLastError();
 }

@@ -141,8 +141,8 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
 // Most keys one top-K call handles per thread (kMaxKpt * 256 = 8192 blocks).
 constexpr int kMaxKpt = 32;
 // Scratch `red` (LDS ints): [2][kWaves][4] counts (eviction), four spare
-// ints (the fused step keeps a flag in the second), [2][kMaxKpt][kWaves]
-// compaction counts, then three 256-bin radix histograms.
+// ints, [2][kMaxKpt][kWaves] compaction counts, then three 256-bin radix
+// histograms.
 constexpr int kRedHist = 2 * kWaves * 4 + 4 + 2 * kMaxKpt * kWaves;
 constexpr int kRedInts = kRedHist + 3 * 256;
 

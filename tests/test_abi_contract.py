@@ -115,8 +115,8 @@ def test_layer_step_workspace_contract(L):
     assert L.layer_step_workspace_bytes(short) == 0
     long = shape(max_blocks=8192, k_resident=128, batch=64, n_kv_heads=8, n_q_heads=32)
     need = L.layer_step_workspace_bytes(long)
-    parts, units = 1 + 8192 // 2048, 64 * 8          # attention part + 2048-block scan parts
-    assert need >= units * 4 + units * parts * 4 + 2 * units * parts * 128 * 4
+    parts, units = 1 + 8192 // 1024, 64 * 8          # attention part + 1024-block scan parts
+    assert need >= units * parts * 4 + 2 * units * parts * 128 * 4
     assert need < 5 * 2**20
     p = ctypes.c_void_p(4096)
     args = [p] * 4 + [0.0, 1, 6] + [p] * 8

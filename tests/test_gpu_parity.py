@@ -254,8 +254,9 @@ def test_fused_step_equals_separate_calls(case):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_fused_step_split_scan_equals_separate_calls(dtype):
-    # contexts past 1024 blocks split the scan over several workgroups that
-    # merge their lists; the result must equal one workgroup's (separate calls)
+    # contexts past 1024 blocks split the scan over several workgroups whose
+    # lists a second launch merges; the result must equal one workgroup's
+    # (separate calls)
     cfg = small(dtype=dtype, batch=4, k_resident=128, n_q_heads=8, n_kv_heads=2, planted=0)
     ctx = [131072, 40000, 16 * 1024 + 1, 900]
     ctx, nbmax, rec, q = setup(cfg, ctx, seed=12)
@@ -266,14 +267,13 @@ def test_fused_step_split_scan_equals_separate_calls(dtype):
         L.summarize(rec)
         L.set_state(*state)
         L.pool.copy_(pool_from_records(rec, L.p2l))
-    for step in (4, 5, 6):          # the workspace counters must reset between launches
+    for step in (4, 5, 6):          # repeated launches reuse the workspace
         a.step(q, step)
         b.step_unfused(q, step)
         torch.cuda.synchronize()
         for name in ("out", "topk_idx", "topk_score", "l2p", "p2l", "last_sel", "admit",
                      "admit_count"):
             assert torch.equal(getattr(a, name), getattr(b, name)), (step, name)
-    assert int(a.workspace[:4 * cfg.batch * cfg.n_kv_heads].view(torch.int32).abs().sum()) == 0
 
 
 def oracle_step(cfg, rec, q, ctx, state, step, m):
