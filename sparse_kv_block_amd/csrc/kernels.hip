@@ -407,10 +407,12 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   if (!whole) {
     if (part == 0) attention();
     else kk = scan_select();
-  } else if (IL && kMfma && RT == 1) {
+  } else if (IL && kMfma) {
     // one pass streams the unit's blocks and its summary records together
-    if constexpr (IL && kMfma && RT == 1) {
-      attn_scan_unit_bf16<D, 1, 2, 8, 1>(
+    // (one summary group per block step with 32 rows: two would not fit
+    // 2 waves per SIMD)
+    if constexpr (IL && kMfma) {
+      attn_scan_unit_bf16<D, RT, (RT == 1 ? 2 : 1), 8, RT>(
           sh, q, pool, p2l, summ + (size_t)unit * sh.NBmax * 2 * D, nb, b, h, L, scale, out,
           reinterpret_cast<float*>(smem), p.keys);
       __syncthreads();
@@ -732,19 +734,18 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
     const float sl = sc * kLog2e;
     // One scan part per unit: attention and scan interleaved in one pass (at
-    // 2 waves per SIMD); with 32 rows the wave holds both row tiles and the
-    // phases stay separate (the interleaved loop would not fit 2 waves per
-    // SIMD).  Split scans: separate phases with a 6-deep scan
-    // unroll, which fits 3 waves per SIMD, the better trade when many short
-    // workgroups share the CUs.
+    // 2 waves per SIMD; with 32 rows the wave holds both row tiles and takes
+    // one summary group per block step).  Split scans: separate phases with
+    // a 6-deep scan unroll, which fits 3 waves per SIMD, the better trade
+    // when many short workgroups share the CUs.
 #define OASIS_STEP(D_, RT_, U_, IL_)                                                            \
   hipLaunchKernelGGL((layer_step_kernel<uint16_t, D_, RT_, U_, IL_>), grid, dim3(kThreads), lds, \
                      st, sh, (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ,   \
                      ctx, sl, step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l,   \
                      last_sel, admit, admit_count, parts, ws)
     if (parts == 1) {
-      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 8, true); else OASIS_STEP(128, 2, 8, false); }
-      else             { if (rt == 1) OASIS_STEP(64, 1, 8, true);  else OASIS_STEP(64, 2, 8, false); }
+      if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 8, true); else OASIS_STEP(128, 2, 8, true); }
+      else             { if (rt == 1) OASIS_STEP(64, 1, 8, true);  else OASIS_STEP(64, 2, 8, true); }
     } else {
       if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 6, false); else OASIS_STEP(128, 2, 6, false); }
       else             { if (rt == 1) OASIS_STEP(64, 1, 6, false);  else OASIS_STEP(64, 2, 6, false); }

@@ -192,8 +192,9 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     // lane l holds digits 255-4l .. 252-4l (descending); inclusive prefix of
     // their counts over the lanes
     const int4 c4 = *reinterpret_cast<const int4*>(hb + 252 - 4 * lane);
-    const int c[4] = {c4.w, c4.z, c4.y, c4.x};            // digits 255-4l, 254-4l, ...
-    const int sum = c[0] + c[1] + c[2] + c[3];
+    // counts of digits 255-4l, 254-4l, 253-4l, 252-4l
+    const int ca = c4.w, cb = c4.z, cc = c4.y, cd = c4.x;
+    const int sum = ca + cb + cc + cd;
     int incl = sum;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -203,12 +204,20 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     const int excl = incl - sum;
     const uint64_t cross = ballot(excl < rem && incl >= rem);
     const int L = __builtin_ctzll(cross);
+    // within the crossing lane: the digit where the count reaches rem, and
+    // the count of larger keys above it
     int above = excl, q = 0;
-    bool found = false;
-#pragma unroll
-    for (int e = 0; e < 3; ++e) {
-      found = found || above + c[e] >= rem;
-      if (!found) { above += c[e]; q = e + 1; }
+    if (above + ca < rem) {
+      above += ca;
+      q = 1;
+      if (above + cb < rem) {
+        above += cb;
+        q = 2;
+        if (above + cc < rem) {
+          above += cc;
+          q = 3;
+        }
+      }
     }
     const int digit = __shfl(255 - 4 * lane - q, L);
     rem -= __shfl(above, L);
