@@ -386,17 +386,33 @@ __device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int s
   a = a < 0 ? 0 : a;
   if (tid < ((K + 1) & ~1) - K) x.vkey[K + tid] = ~0ull;   // pad to an even count
   __syncthreads();
-  if (elig) {
-    int rank = 0;
+  // rank every eligible key among all K: P threads per candidate, each over
+  // 1/P of the list (all four waves busy), partial counts summed through LDS
+  {
+    const int P = K <= kThreads / 4 ? 4 : (K <= kThreads / 2 ? 2 : 1);
+    const int span = kThreads / P;
+    const int c = tid % span, part = tid / span;
     const int K2 = (K + 1) >> 1;
-#pragma unroll 4
-    for (int p = 0; p < K2; ++p) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(x.vkey)[p];
-      const uint64_t a0 = ((uint64_t)v[1] << 32) | v[0];
-      const uint64_t a1 = ((uint64_t)v[3] << 32) | v[2];
-      rank += (a0 < key) + (a1 < key);
+    const int p0 = part * K2 / P, p1 = (part + 1) * K2 / P;
+    int rank = 0;
+    uint64_t ck = ~0ull;
+    if (c < K) {
+      ck = x.vkey[c];
+#pragma unroll 8
+      for (int p = p0; p < p1; ++p) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(x.vkey)[p];
+        const uint64_t a0 = ((uint64_t)v[1] << 32) | v[0];
+        const uint64_t a1 = ((uint64_t)v[3] << 32) | v[2];
+        rank += (a0 < ck) + (a1 < ck);
+      }
     }
-    if (rank < a) x.victim[rank] = tid;
+    int* prt = x.red + kRedHist;                       // the radix histograms are free here
+    if (part > 0 && c < K) prt[(part - 1) * span + c] = rank;
+    __syncthreads();
+    if (part == 0 && c < K && ck != ~0ull) {
+      for (int q = 1; q < P; ++q) rank += prt[(q - 1) * span + c];
+      if (rank < a) x.victim[rank] = c;
+    }
   }
   __syncthreads();
   // 3. apply
