@@ -487,9 +487,10 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(
     total += n;
   }
   __syncthreads();
-  // up to (8192 / kScanChunk) lists of K <= 256 entries: at most 8192 keys
-  const int kk = topk_unit<kMaxKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                    p.cand_key, p.ev.red);
+  // at most 8192 / kScanChunk lists of K <= 256 entries
+  constexpr int kMergeKpt = (8192 / kScanChunk) * 256 / kThreads;
+  const int kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                      p.cand_key, p.ev.red);
   for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
   __syncthreads();
   for (int t = tid; t < sh.K; t += kThreads) {
