@@ -252,12 +252,13 @@ def test_fused_step_equals_separate_calls(case):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_fused_step_split_scan_equals_separate_calls(dtype):
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 128), ("bf16", 256)])
+def test_fused_step_split_scan_equals_separate_calls(dtype, K):
     # contexts past 1024 blocks split the scan over several workgroups whose
     # lists a second launch merges; the result must equal one workgroup's
     # (separate calls)
-    cfg = small(dtype=dtype, batch=4, k_resident=128, n_q_heads=8, n_kv_heads=2, planted=0)
+    # K = 256 at 8192 blocks: the merge sees its largest input, 8 lists of 256
+    cfg = small(dtype=dtype, batch=4, k_resident=K, n_q_heads=8, n_kv_heads=2, planted=0)
     ctx = [131072, 40000, 16 * 1024 + 1, 900]
     ctx, nbmax, rec, q = setup(cfg, ctx, seed=12)
     assert lib.layer_step_workspace_bytes(lib.Shape.of(cfg, nbmax)) > 0
