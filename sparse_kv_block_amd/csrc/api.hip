@@ -32,6 +32,9 @@ oasis_status hip_status(hipError_t e, const char* what) {
 constexpr int kMaxBlocks = 8192;
 constexpr int kMaxK = 256;
 constexpr int kMaxGroup = 16;
+// Units per call: keeps every per-launch count the kernels form in 32-bit
+// ints (units x 256 slots, units x 9 scan parts, units x 64 dense chunks).
+constexpr int kMaxUnits = 1 << 22;
 
 oasis_status check_shape(const oasis_shape* s, const char* fn) {
   if (!s) return fail(OASIS_ERR_INVALID, "%s: shape is NULL", fn);
@@ -58,8 +61,9 @@ oasis_status check_shape(const oasis_shape* s, const char* fn) {
     return fail(OASIS_ERR_UNSUPPORTED, "%s: k_resident %d (at most %d)", fn, s->k_resident, kMaxK);
   if (s->dtype != OASIS_DTYPE_F32 && s->dtype != OASIS_DTYPE_BF16)
     return fail(OASIS_ERR_UNSUPPORTED, "%s: dtype %d", fn, s->dtype);
-  if ((long long)s->batch * s->n_kv_heads > 0x7FFFFFFFLL)
-    return fail(OASIS_ERR_UNSUPPORTED, "%s: too many units", fn);
+  if ((long long)s->batch * s->n_kv_heads > kMaxUnits)
+    return fail(OASIS_ERR_UNSUPPORTED, "%s: %lld units (batch x KV heads, at most %d)", fn,
+                (long long)s->batch * s->n_kv_heads, kMaxUnits);
   return OASIS_OK;
 }
 

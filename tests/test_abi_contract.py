@@ -62,6 +62,7 @@ def shape(**kw):
     (dict(k_resident=257), 2),
     (dict(n_q_heads=34, n_kv_heads=2), 2),
     (dict(dtype=7), 2),
+    (dict(batch=(1 << 21) + 1, n_kv_heads=2, n_q_heads=2), 2),     # more than 2^22 units
 ])
 def test_bad_shapes_are_rejected(L, kw, status):
     raw = L.raw()
