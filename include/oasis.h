@@ -19,8 +19,9 @@
  *  per KV head, 1 <= G <= 16), head dim d in {64, 128}, block size S = 16
  *  tokens, NBmax logical blocks per (request, KV head) in the record and
  *  summary arrays (1 <= NBmax <= 8192), K resident slots per (request, KV
- *  head) (1 <= K <= 256), at most 2^22 units (B * Hkv).  Request b has ctx_len[b] valid tokens; its logical
- *  blocks are j < NB_b = min(ceil(ctx_len[b] / 16), NBmax).  A "unit" is one
+ *  head) (1 <= K <= 256), at most 2^22 units (B * Hkv).  Request b has
+ *  ctx_len[b] valid tokens; its logical blocks are
+ *  j < NB_b = min(ceil(ctx_len[b] / 16), NBmax).  A "unit" is one
  *  (request, KV head) pair, numbered b * Hkv + h.
  *
  *  Element type.  OASIS_DTYPE_F32 or OASIS_DTYPE_BF16 for queries, records,
