@@ -121,6 +121,67 @@ def dense_leg(cfg, layer, rec_host, q, reps: int = 10):
             "hbm_kv_per_layer_GiB": round(kv / 2**30, 2)}
 
 
+def kernels_leg(cfg, layer, ctx, nbmax, qs, reps: int = 10):
+    """Each standalone kernel of the step on the timed layer's state, timed
+    with HIP events on the current stream (median of `reps`), against its
+    algorithmic bytes: summarize (reads every key of the full KV, here a
+    device-resident copy), look-ahead attention (the resident pool),
+    summary scan + top-K (the summaries), capped eviction (maps only)."""
+    import torch
+    from sparse_kv_block_amd import gen, lib
+    stream = torch.cuda.current_stream()
+    sh = layer.shape
+    es = 2 if cfg.dtype == "bf16" else 4
+    units = cfg.batch * cfg.n_kv_heads
+    nb = np.minimum((ctx.astype(np.int64) + 15) // 16, nbmax)
+    sum_blocks = int(nb.sum()) * cfg.n_kv_heads
+
+    def timed(fn, restore=None):
+        fn()
+        ts = []
+        for _ in range(reps):
+            if restore:
+                restore()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+
+    out = {}
+    rec = gen.records(cfg, ctx, nbmax, device=layer.device)
+    summ = torch.empty_like(layer.summ)
+    us = timed(lambda: lib.summarize(sh, rec, layer.ctx_len, summ))
+    byt = sum_blocks * (16 * cfg.head_dim * es + 2 * cfg.head_dim * es)
+    out["summarize"] = {"us": round(us, 1), "bytes": byt, "GBps": round(byt / us / 1e3, 1)}
+    del rec, summ
+    torch.cuda.empty_cache()
+    q = qs[0]
+    us = timed(lambda: lib.lookahead_attn(sh, q, layer.pool, layer.p2l, layer.ctx_len, layer.out))
+    byt = units * cfg.k_resident * 2 * 16 * cfg.head_dim * es + 2 * q.numel() * es
+    out["lookahead_attn"] = {"us": round(us, 1), "bytes": byt, "GBps": round(byt / us / 1e3, 1)}
+    us = timed(lambda: lib.score_topk(sh, q, layer.summ, layer.ctx_len, layer.topk_idx,
+                                      layer.topk_score, q_row=1))
+    byt = sum_blocks * 2 * cfg.head_dim * es + q.numel() * es // 2 + units * cfg.k_resident * 8
+    out["score_topk"] = {"us": round(us, 1), "bytes": byt, "GBps": round(byt / us / 1e3, 1)}
+    saved = layer.state()
+    m = cfg.max_admit()
+
+    def restore():
+        layer.set_state(*saved)
+
+    us = timed(lambda: lib.capped_evict(sh, layer.topk_idx, 10**6, m, layer.l2p, layer.p2l,
+                                        layer.last_sel, layer.admit, layer.admit_count),
+               restore=restore)
+    restore()
+    out["capped_evict"] = {"us": round(us, 1)}
+    log(f"[bench] kernels: " + ", ".join(f"{k} {v['us']} us" + (f" ({v['GBps']} GB/s)" if 'GBps' in v else "")
+                                         for k, v in out.items()))
+    return out
+
+
 def append_leg(layer, rec_host, reps: int = 8):
     """Decode append of one token per request into the pinned host records
     (written over the host link), the resident copies and the summaries."""
@@ -383,6 +444,8 @@ def main():
                     help="also time the dense comparator (attention over the full HBM-resident KV)")
     ap.add_argument("--append", action="store_true",
                     help="also time the decode append (after every other GPU leg)")
+    ap.add_argument("--kernels", action="store_true",
+                    help="also time each standalone kernel of the step (per-kernel GB/s)")
     ap.add_argument("--capmodel", action="store_true",
                     help="also measure the host-link budget (SDMA copy, K/2 step) and the "
                          "largest cap that hides in a 36-layer step")
@@ -456,6 +519,7 @@ def main():
     wall = time.perf_counter() - t0
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_kernel_s = float(np.mean(kern_ms)) / 1e3
+    median_kernel_us = float(np.median(kern_ms)) * 1e3
     ms_per_step = wall / args.steps * 1e3
     value = args.steps / wall
     algo = algorithmic_bytes(cfg, ctx)
@@ -487,7 +551,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(algo["total"]),
                      "kernel": KERNEL, "algorithmic_bytes_per_launch": algo["total"],
-                     "avg_kernel_us": round(avg_kernel_s * 1e6, 2)},
+                     "avg_kernel_us": round(avg_kernel_s * 1e6, 2),
+                     "median_kernel_us": round(median_kernel_us, 2)},
     }
 
     if not args.no_pcie:
@@ -526,6 +591,8 @@ def main():
     if args.pipeline:
         result["pipeline_36_layer"] = pipeline_leg(layer, rec_host, args.pipeline_steps, 2)
 
+    if args.kernels:
+        result["per_kernel"] = kernels_leg(cfg, layer, ctx, nbmax, qs)
     if args.capmodel:
         if "pcie" not in result:
             log("[bench] --capmodel needs the prefetch leg (drop --no-pcie)")
