@@ -62,6 +62,43 @@ struct Elem<float> {
   __device__ static __forceinline__ float one(const float* p) { return *p; }
 };
 
+// N consecutive elements held as raw 32-bit words: loaded with nontemporal
+// vector loads, unpacked to fp32 later.  Hot loops issue all their loads
+// first, unconditionally (out-of-range items load a clamped, in-range
+// address and are ignored afterwards), and unpack after: no branch and no
+// use sits between a load and the loads issued after it, so the compiler's
+// wait counts stay exact and the loads stay in flight together.
+template <typename T, int N>
+struct Raw {
+  static constexpr int W = N * (int)sizeof(T) / 4;
+  static_assert(W == 2 || W % 4 == 0, "16- or 8-byte vectors");
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const T* p) {
+    if constexpr (W == 2) {
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      w[0] = v[0];
+      w[1] = v[1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
+        w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+      }
+    }
+  }
+  __device__ __forceinline__ void unpack(float* v) const {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        v[2 * i] = bf16_lo(w[i]);
+        v[2 * i + 1] = bf16_hi(w[i]);
+      } else {
+        v[i] = __uint_as_float(w[i]);
+      }
+    }
+  }
+};
+
 // Halved group sums of the query row over the G query heads of KV head h, for
 // channels c0 .. c0+CPL: Qh = sum_i q_ic / 2, Ah = sum_i |q_ic| / 2.
 template <typename T, int D, int CPL>
@@ -112,25 +149,22 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
   float Qh[CPL], Ah[CPL];
   group_query_sums<T, D, CPL>(sh, q, q_row, b, h, c0, Qh, Ah);
 
+  const T* last = summ_unit + (size_t)(nb > 0 ? nb - 1 : 0) * 2 * D + c0;
   for (int jb = w * 4; jb < nb; jb += kThreads / 16 * U) {
-    float part[U];
+    Raw<T, CPL> lo[U], hi[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jb + quad + (kThreads / 16) * u;
-      float lo[CPL], hi[CPL];
-      if (j < nb) {
-        const T* rec = summ_unit + (size_t)j * 2 * D + c0;
-        Elem<T>::template load<CPL>(rec, lo);
-        Elem<T>::template load<CPL>(rec + D, hi);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) { lo[c] = 0.f; hi[c] = 0.f; }
-      }
-      part[u] = record_part<CPL>(lo, hi, Qh, Ah);
+      const T* rec = j < nb ? summ_unit + (size_t)j * 2 * D + c0 : last;
+      lo[u].load(rec);
+      hi[u].load(rec + D);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float s = row16_sum(part[u]);
+      float fl[CPL], fh[CPL];
+      lo[u].unpack(fl);
+      hi[u].unpack(fh);
+      const float s = row16_sum(record_part<CPL>(fl, fh, Qh, Ah));
       const int j = jb + quad + (kThreads / 16) * u;
       if (n == 0 && j < nb) keys[j] = score_key(s);
     }
