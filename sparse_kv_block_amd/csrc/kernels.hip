@@ -17,6 +17,7 @@ namespace oasis {
 // ------------------------------------------------------------------ summaries
 // One wave per block: lane (g, n) takes channels n*D/16 .. +D/16 of tokens
 // g, g+4, g+8, g+12; the four token groups are merged with lane exchanges.
+// The records may be host-mapped memory.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void summarize_kernel(Shape sh, const T* __restrict__ rec,
                                                              const int32_t* __restrict__ ctx,
@@ -38,15 +39,20 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(Shape sh, const T* 
   float mn[CPL], mx[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) { mn[c] = INFINITY; mx[c] = -INFINITY; }
+  // all four loads first (a token past the context re-reads the last valid
+  // one, which leaves min and max unchanged), then the reductions
+  Raw<T, CPL> r[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = g + 4 * i;
-    if (u < nv) {
-      float v[CPL];
-      Elem<T>::template load<CPL>(blk + u * D + c0, v);
+    r[i].load(blk + (u < nv ? u : nv - 1) * D + c0);
+  }
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) { mn[c] = fminf(mn[c], v[c]); mx[c] = fmaxf(mx[c], v[c]); }
-    }
+  for (int i = 0; i < 4; ++i) {
+    float v[CPL];
+    r[i].unpack(v);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) { mn[c] = fminf(mn[c], v[c]); mx[c] = fmaxf(mx[c], v[c]); }
   }
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
