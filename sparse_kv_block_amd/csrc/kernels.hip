@@ -481,16 +481,28 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(
   const SelectPtrs p = select_ptrs(smem, 0, sh.K);
   uint32_t* mkey = reinterpret_cast<uint32_t*>(smem + SelectLds(0, sh.K).total);
   int* midx = reinterpret_cast<int*>(mkey + parts * sh.K);
+  // every part's length at once, then all entries in one pass (loads issued
+  // unconditionally; entries past a list's length are not stored)
+  int* lens = p.ev.red;                       // the eviction's counters are free here
+  const int np = active - 1;                  // scan parts, 1 .. 8
+  if (tid < np) {
+    const int n = ws.n[(size_t)unit * parts + 1 + tid];
+    lens[tid] = n < 0 ? 0 : (n > sh.K ? sh.K : n);
+  }
+  __syncthreads();
   int total = 0;
-  for (int pp = 1; pp < active; ++pp) {
-    const size_t sl = (size_t)unit * parts + pp;
-    int n = ws.n[sl];
-    n = n < 0 ? 0 : (n > sh.K ? sh.K : n);
-    for (int r = tid; r < n; r += kThreads) {
-      mkey[total + r] = ws.key[sl * sh.K + r];
-      midx[total + r] = ws.idx[sl * sh.K + r];
+  for (int pp = 0; pp < np; ++pp) total += lens[pp];
+  for (int e = tid; e < np * sh.K; e += kThreads) {
+    const int pp = e / sh.K, r = e % sh.K;
+    const size_t sl = (size_t)unit * parts + 1 + pp;
+    const uint32_t k = ws.key[sl * sh.K + r];
+    const int i = ws.idx[sl * sh.K + r];
+    int off = 0;
+    for (int x = 0; x < pp; ++x) off += lens[x];
+    if (r < lens[pp]) {
+      mkey[off + r] = k;
+      midx[off + r] = i;
     }
-    total += n;
   }
   __syncthreads();
   // at most 8192 / kScanChunk lists of K <= 256 entries
