@@ -39,19 +39,18 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Qh, Ah);
   const int Gw = nb > 4 * w ? (nb - 4 * w + 15) / 16 : 0;   // this wave's record groups
 
+  // Group loads are issued unconditionally (a group past the end loads a
+  // clamped in-range record and is ignored): a branch around a load makes
+  // the compiler wait for loads issued after it as well.
   using Row = uint32_t __attribute__((ext_vector_type(RW)));
   auto load_groups = [&](int t, int cnt, Row* lo, Row* hi) {
 #pragma unroll
     for (int k = 0; k < cnt; ++k) {
-      const int j = 16 * (t + k) + 4 * w + quad;
-      if (t + k < Gw && j < nb) {
-        const uint16_t* rec = summ_unit + (size_t)j * 2 * D + c0;
-        lo[k] = __builtin_nontemporal_load(reinterpret_cast<const Row*>(rec));
-        hi[k] = __builtin_nontemporal_load(reinterpret_cast<const Row*>(rec + D));
-      } else {
-        lo[k] = Row(0u);
-        hi[k] = Row(0u);
-      }
+      int j = 16 * (t + k) + 4 * w + quad;
+      j = (t + k < Gw && j < nb) ? j : (nb > 0 ? nb - 1 : 0);
+      const uint16_t* rec = summ_unit + (size_t)j * 2 * D + c0;
+      lo[k] = __builtin_nontemporal_load(reinterpret_cast<const Row*>(rec));
+      hi[k] = __builtin_nontemporal_load(reinterpret_cast<const Row*>(rec + D));
     }
   };
   auto score_groups = [&](int t, int cnt, const Row* lo, const Row* hi) {
