@@ -203,15 +203,20 @@ def test_attention_scale_argument():
 
 
 # --------------------------------------------------------------------------- prefetch
+# (batch, admissions per unit): the gather grid follows the item count (one
+# workgroup per 32 items between 32 and 128, at least two items per group),
+# so these cover 3 workgroups, 15 and 64.
+@pytest.mark.parametrize("batch,m", [(3, 5), (3, 1), (64, 16)])
 @pytest.mark.parametrize("mode", ["gather", "memcpy"])
 @pytest.mark.parametrize("src", ["pinned", "device"])
-def test_prefetch(mode, src):
-    cfg = small(batch=3, k_resident=16)
-    ctx, nbmax, rec, q = setup(cfg, [1000, 500, 40], seed=8, device="cpu")
+def test_prefetch(mode, src, batch, m):
+    cfg = small(batch=batch, k_resident=16)
+    ctxs = [1000, 500, 40] if batch == 3 else [1000 - 13 * i for i in range(batch)]
+    ctx, nbmax, rec, q = setup(cfg, ctxs, seed=8, device="cpu")
     l2p, p2l, ls = [x.numpy() for x in gen.random_state(cfg, ctx, nbmax, 8, fill=0.7)]
     scores = np.random.default_rng(8).normal(size=(cfg.batch, cfg.n_kv_heads, nbmax))
     T, _ = oracle.topk(scores, ctx, 16, cfg.k_resident)
-    admit, count = oracle.capped_evict(T, 3, 5, l2p, p2l, ls)
+    admit, count = oracle.capped_evict(T, 3, m, l2p, p2l, ls)
     layer = Layer(cfg, ctx, nbmax)
     layer.pool.fill_(3)
     layer.admit.copy_(torch.from_numpy(admit))
@@ -223,7 +228,7 @@ def test_prefetch(mode, src):
     before.record()
     staging = torch.empty(cfg.batch * cfg.n_kv_heads * (3 * cfg.k_resident + 1), dtype=torch.int32,
                           pin_memory=True)
-    layer.prefetch(records, 5, mode=lib.GATHER if mode == "gather" else lib.MEMCPY,
+    layer.prefetch(records, m, mode=lib.GATHER if mode == "gather" else lib.MEMCPY,
                    host_staging=staging, side_stream=side, wait_before=before, done=done)
     torch.cuda.current_stream().wait_event(done)
     torch.cuda.synchronize()
