@@ -48,7 +48,7 @@ struct AttnWave {
   static constexpr int NT = D / 16;   // output tiles
   static constexpr int REC = 2 * kBlock * D;
   static constexpr bool kPairs = RT == 2 && TW == 1;   // waves paired on a slot half
-  static constexpr int NSPLIT = kPairs ? 2 : kWaves;
+  static constexpr int NSPLIT = kPairs ? kWaves / 2 : kWaves;
 
   int w, g, n, rt, split;
   bf16x8 qop[TW][KS];
@@ -212,8 +212,9 @@ struct AttnWave {
       }
     }
     // waves 0,1 write their scaled partial outputs into buffer pair slot w&1;
-    // waves 2,3 add theirs.  Paired waves: buffer slot = row tile.
-    for (int phase = 0; phase < 2; ++phase) {
+    // waves 2,3 add theirs, then 4,5 and so on.  Paired waves: buffer slot =
+    // row tile.
+    for (int phase = 0; phase < kWaves / 2; ++phase) {
       if ((w >> 1) == phase) {
 #pragma unroll
         for (int t = 0; t < TW; ++t) {

@@ -47,6 +47,35 @@ __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Integer DPP move; lanes whose source is outside the row (or whose row is
+// not in ROWS) get 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts inside each
+// 16-lane row, then the row totals broadcast into the rows above.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += dpp_i<0x111>(x);        // row_shr:1
+  x += dpp_i<0x112>(x);        // row_shr:2
+  x += dpp_i<0x114>(x);        // row_shr:4
+  x += dpp_i<0x118>(x);        // row_shr:8
+  x += dpp_i<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_i<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Bitwise OR over the 64 lanes of a wave (a wave-uniform value).
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+  x |= (uint32_t)dpp_i<0xB1>((int)x);    // quad_perm [1,0,3,2]
+  x |= (uint32_t)dpp_i<0x4E>((int)x);    // quad_perm [2,3,0,1]
+  x |= (uint32_t)dpp_i<0x141>((int)x);   // row_half_mirror
+  x |= (uint32_t)dpp_i<0x140>((int)x);   // row_mirror
+  return (uint32_t)(__builtin_amdgcn_readlane((int)x, 0) | __builtin_amdgcn_readlane((int)x, 16) |
+                    __builtin_amdgcn_readlane((int)x, 32) | __builtin_amdgcn_readlane((int)x, 48));
+}
+
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]

@@ -13,9 +13,9 @@
 // Summary loads are nontemporal (read once per step).  The scores of the
 // unit's whole context stay in LDS as order-preserving 32-bit keys.
 //
-// Top-K: MSB-first radix bisection on the keys, counting with wave ballots
-// (popcount) and one LDS exchange per bit, finds the K-th largest key T; keys
-// above T and the lowest-index keys equal to T are compacted and ranked by
+// Top-K: radix selection on the keys (eight bits per round, from the highest
+// bit on which the keys differ) finds the K-th largest key T; keys above T
+// and the lowest-index keys equal to T are compacted and ranked by
 // (score desc, block asc).
 //
 // Capped eviction (same page: admissions per step are capped and each
@@ -174,186 +174,217 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
 // ---------------------------------------------------------------- top-K
 // Most keys one top-K call handles per thread (kMaxKpt * 256 = 8192 blocks).
 constexpr int kMaxKpt = 32;
-// Scratch `red` (LDS ints): [2][kWaves][4] counts (eviction), four spare
-// ints, [2][kMaxKpt][kWaves] compaction counts, then three 256-bin radix
-// histograms.
+// Scratch `red` (LDS ints): [2][kWaves][4] counts (eviction; the top-K
+// exchanges its per-wave OR reductions there), four spare ints,
+// [2][kMaxKpt][kWaves] top-K compaction counts (then its partial ranks), then
+// three 256-bin radix histograms.
 constexpr int kRedHist = 2 * kWaves * 4 + 4 + 2 * kMaxKpt * kWaves;
 constexpr int kRedInts = kRedHist + 3 * 256;
 
 // Selects the min(K, nb) best keys; writes sel_idx[0..kk) / sel_key[0..kk) in
 // (key desc, index asc) order and returns kk.  cand_* are (K + 4)-entry
-// scratch.  Requires nb <= KPT * kThreads.  Thread t holds keys t, t + 256,
+// scratch.  Requires nb <= KPT * kThreads.  Thread t holds keys t, t + kThreads,
 // ... in registers for the whole selection.
+//
+// 1. The K-th largest key T: the bits all keys share are found first (wave
+//    OR reductions of the keys and of their complements); then radix
+//    selection eight bits at a time from the highest differing bit: the keys
+//    that match the digits chosen so far are counted per next digit in an
+//    LDS histogram (one barrier per round) and every wave finds, on its own,
+//    the digit at which the count of larger keys reaches kk (a DPP prefix sum
+//    over 4 digits per lane).  Three histograms rotate so that clearing one
+//    never races with the use of another.  When the chosen digit's count
+//    equals the number still needed, every key at or above the prefix is
+//    selected and the search stops early with no ties.  Key 0 is never a
+//    score key (score_key maps every finite score above it) and marks the
+//    padding.
+// 2. Compaction in index order (chunk, wave, lane), from one packed
+//    (above, tied) count per chunk and wave: keys above T go to cand_*, the
+//    lowest-index ties straight to the end of the sorted list.
+// 3. Ranking of the keys above T by (key desc, position asc).
 template <int KPT>
 __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, int* sel_idx,
                                          uint32_t* sel_key, int* cand_idx, uint32_t* cand_key,
                                          int* red) {
   static_assert(KPT >= 1 && KPT <= kMaxKpt, "keys per thread");
   const int tid = threadIdx.x;
-  const int w = tid / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
   const int kk = K < nb ? K : nb;
   if (kk <= 0) return 0;
-  const int act = (nb + kThreads - 1) / kThreads;   // chunks holding keys (uniform)
+  const int act = (nb + kThreads - 1) / kThreads;
   uint32_t k[KPT];
+  uint32_t kor = 0u, knand = 0u;       // OR of the keys, OR of their complements
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int j = i * kThreads + tid;
     k[i] = (i < act && j < nb) ? keys[j] : 0u;
+    if (k[i] != 0u) { kor |= k[i]; knand |= ~k[i]; }
   }
-  // 1. K-th largest key T = max{v : #{key >= v} >= kk} by radix selection,
-  //    eight bits per round from the top: the keys that match the digits
-  //    chosen so far are counted per next digit in an LDS histogram (one
-  //    barrier per round); then every wave finds, on its own, the digit at
-  //    which the count of larger keys reaches kk.  Three histograms rotate
-  //    so that clearing one never races with the use of another.  Key 0 is
-  //    never a score key (score_key maps every finite score above it) and
-  //    marks the padding.
+  // the bits every key shares need no radix round
   int* hist = red + kRedHist;
-  const int lane = lane_id();
-  hist[tid] = 0;
-  hist[kThreads + tid] = 0;
+  int* xw = red;                                       // [2][kWaves]: the eviction's counters
+  for (int e = tid; e < 2 * 256; e += kThreads) hist[e] = 0;
+  {
+    const uint32_t o = wave_or(kor), n = wave_or(knand);
+    if (lane == 0) { xw[w] = (int)o; xw[kWaves + w] = (int)n; }
+  }
   __syncthreads();
-  uint32_t T = 0, mask = 0;
+  uint32_t allor = 0u, allnand = 0u;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) { allor |= (uint32_t)xw[v]; allnand |= (uint32_t)xw[kWaves + v]; }
+  const uint32_t diff = allor & allnand;               // bits that differ between keys
+  const int hb = diff ? 31 - __builtin_clz(diff) : -1; // highest differing bit
+  uint32_t mask = hb < 0 ? ~0u : (hb >= 31 ? 0u : ~((2u << hb) - 1u));
+  uint32_t T = allor & mask;
   int rem = kk;
+  bool ge = false;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int shift = 24 - 8 * r;
-    int* hb = hist + (r % 3) * 256;
+    const int shift = hb - 7 - 8 * r;                  // digit bits shift+7 .. shift (may be < 0)
+    if (shift + 7 < 0) break;
+    int* hbuf = hist + (r % 3) * 256;
+    const uint32_t dm = shift >= 0 ? (255u << shift) : (255u >> -shift);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (i < act && k[i] != 0u && (k[i] & mask) == T) atomicAdd(&hb[(k[i] >> shift) & 255u], 1);
+    for (int i = 0; i < KPT; ++i) {
+      if (i < act) {
+        const bool m = k[i] != 0u && (k[i] & mask) == T;
+        const int d = (int)(shift >= 0 ? (k[i] >> shift) & 255u : (k[i] << -shift) & 255u);
+        if (m) atomicAdd(&hbuf[d], 1);
+      }
+    }
     __syncthreads();
-    // lane l holds digits 255-4l .. 252-4l (descending); inclusive prefix of
-    // their counts over the lanes
-    const int4 c4 = *reinterpret_cast<const int4*>(hb + 252 - 4 * lane);
-    // counts of digits 255-4l, 254-4l, 253-4l, 252-4l
+    const int4 c4 = *reinterpret_cast<const int4*>(hbuf + 252 - 4 * lane);
     const int ca = c4.w, cb = c4.z, cc = c4.y, cd = c4.x;
     const int sum = ca + cb + cc + cd;
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      incl += lane >= o ? v : 0;
-    }
+    const int incl = wave_incl_sum(sum);
     const int excl = incl - sum;
     const uint64_t cross = ballot(excl < rem && incl >= rem);
     const int L = __builtin_ctzll(cross);
-    // within the crossing lane: the digit where the count reaches rem, and
-    // the count of larger keys above it
-    int above = excl, q = 0;
+    int above = excl, q = 0, cq = ca;
     if (above + ca < rem) {
-      above += ca;
-      q = 1;
+      above += ca; q = 1; cq = cb;
       if (above + cb < rem) {
-        above += cb;
-        q = 2;
+        above += cb; q = 2; cq = cc;
         if (above + cc < rem) {
-          above += cc;
-          q = 3;
+          above += cc; q = 3; cq = cd;
         }
       }
     }
-    const int digit = __shfl(255 - 4 * lane - q, L);
-    rem -= __shfl(above, L);
-    T |= (uint32_t)digit << shift;
-    mask |= 255u << shift;
-    hist[((r + 2) % 3) * 256 + tid] = 0;                    // for round r + 2
-  }
-  // 2. compact in index order (chunk, wave, lane): every key > T, then the
-  //    lowest-index keys == T up to kk.  One barrier: each wave publishes its
-  //    per-chunk counts, every thread then sums the counts before its own.
-  int* cg = red + 2 * kWaves * 4 + 4;
-  int* ce = cg + kMaxKpt * kWaves;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if (i < act) {
-      const int g = __popcll(ballot(k[i] > T));
-      const int e = __popcll(ballot(k[i] == T));
-      if (lane_id() == 0) { cg[i * kWaves + w] = g; ce[i * kWaves + w] = e; }
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(255 - 4 * lane - q, L);
+    rem -= __builtin_amdgcn_readlane(above, L);
+    const int cnt = __builtin_amdgcn_readlane(cq, L);
+    T |= shift >= 0 ? digit << shift : digit >> -shift;
+    mask |= dm;
+    for (int e = tid; e < 256; e += kThreads) hist[((r + 2) % 3) * 256 + e] = 0;
+    if (cnt == rem) {            // every key with this prefix is selected
+      ge = true;
+      break;
     }
   }
+  // compaction
+  int* cnt = red + 2 * kWaves * 4 + 4;
+  uint64_t mgv[KPT], mev[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    mgv[i] = 0; mev[i] = 0;
+    if (i < act) {
+      const bool gt = ge ? (k[i] >= T && k[i] != 0u) : k[i] > T;
+      const bool eq = !ge && k[i] == T;
+      mgv[i] = ballot(gt);
+      mev[i] = ballot(eq);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (i < act && lane == 0) cnt[i * kWaves + w] = (int)((uint32_t)__popcll(mgv[i]) | ((uint32_t)__popcll(mev[i]) << 16));
   __syncthreads();
-  int ngt = 0;
-  for (int x = 0; x < act * kWaves; ++x) ngt += cg[x];
+  constexpr int NP = (KPT * kWaves + 63) / 64;
+  const int nx = act * kWaves;
+  int ex[NP];
+  int carry = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int x = p * 64 + lane;
+    const int c = x < nx ? cnt[x] : 0;
+    const int in = wave_incl_sum(c) + carry;
+    ex[p] = in - c;
+    carry = __builtin_amdgcn_readlane(in, 63);
+  }
+  const int ngt = carry & 0xFFFF;
   const int need = kk - ngt;
-  int run_g = 0, run_e = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     if (i < act) {
-      int og = run_g, oe = run_e;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
-        const int g = cg[i * kWaves + v], e = ce[i * kWaves + v];
-        og += v < w ? g : 0;
-        oe += v < w ? e : 0;
-        run_g += g;
-        run_e += e;
-      }
-      const bool gt = k[i] > T, eq = k[i] == T;
-      const uint64_t mg = ballot(gt), me = ballot(eq);
+      const int o = __builtin_amdgcn_readlane(ex[(i * kWaves) / 64], (i * kWaves) % 64 + w);
       const int j = i * kThreads + tid;
-      if (gt) {
-        const int pos = og + lanes_below(mg);
+      if ((mgv[i] >> lane) & 1ull) {
+        const int pos = (o & 0xFFFF) + lanes_below(mgv[i]);
         cand_idx[pos] = j;
         cand_key[pos] = k[i];
       }
-      if (eq) {
-        const int r = oe + lanes_below(me);
-        if (r < need) {
-          cand_idx[ngt + r] = j;
-          cand_key[ngt + r] = T;
+      if ((mev[i] >> lane) & 1ull) {
+        const int rr = (o >> 16) + lanes_below(mev[i]);
+        if (rr < need) {
+          sel_idx[ngt + rr] = j;
+          sel_key[ngt + rr] = T;
         }
       }
     }
   }
-  // pad to a multiple of 4 so the ranking can read four entries at a time
-  if (tid < ((kk + 3) & ~3) - kk) {
-    cand_key[kk + tid] = 0u;
-    cand_idx[kk + tid] = 0x7FFFFFFF;
-  }
+  if (tid < 3) cand_key[ngt + tid] = 0u;     // padding never ranks above a key
   __syncthreads();
-  // 3. rank the kk candidates by (key desc, index asc).  Up to 128
-  //    candidates: two threads per candidate, each over half of the list.
-  const int kk4 = (kk + 3) >> 2;
-  auto rank_range = [&](uint32_t key, int j, int p0, int p1) {
-    int rank = 0;
+  // rank the ngt keys above the threshold by (key desc, position asc).  P
+  // parts of kThreads / P threads (whole waves) each count over 1/P of the
+  // list; a wave's loop bounds are uniform: positions before all of its
+  // candidates count keys >= key, positions after all of them keys > key,
+  // and only the chunks in between need both tests.
+  constexpr int kLogThreads = __builtin_ctz(kThreads);
+  const int n4 = (ngt + 3) >> 2;
+  const int lp = ngt <= kThreads / 4 ? 2 : (ngt <= kThreads / 2 ? 1 : 0);   // log2 of the parts
+  const int P = 1 << lp;
+  const int span = kThreads >> lp;
+  const int c = tid & (span - 1), part = tid >> (kLogThreads - lp);
+  const int cw0 = (w * kWave) & (span - 1);            // first candidate of the wave
+  const int pw = (w * kWave) >> (kLogThreads - lp);    // the wave's part
+  const int p0 = (pw * n4) >> lp, p1 = ((pw + 1) * n4) >> lp;
+  const int pa = min(max(p0, cw0 >> 2), p1);
+  const int pb = max(pa, min(p1, ((cw0 + kWave - 1) >> 2) + 1));
+  const uint32_t key = c < ngt ? cand_key[c] : 0u;
+  const uint32_t km = key - 1u;
+  int rank = 0;
 #pragma unroll 4
-    for (int p = p0; p < p1; ++p) {
-      const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
-      const u32x4 jp = reinterpret_cast<const u32x4*>(cand_idx)[p];
+  for (int p = p0; p < pa; ++p) {
+    const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rank += (kp[e] > key) || (kp[e] == key && (int)jp[e] < j);
-    }
-    return rank;
-  };
-  if (kk <= kThreads / 2) {
-    const int c = tid % (kThreads / 2), half = tid / (kThreads / 2);
-    const int h4 = (kk4 + 1) >> 1;
-    int rank = 0;
-    uint32_t key = 0;
-    int j = 0;
-    if (c < kk) {
-      key = cand_key[c];
-      j = cand_idx[c];
-      rank = half ? rank_range(key, j, h4, kk4) : rank_range(key, j, 0, h4);
-    }
-    if (half && c < kk) cg[c] = rank;                 // compaction counts are spent
+    for (int e = 0; e < 4; ++e) rank += kp[e] > km;
+  }
+#pragma unroll 4
+  for (int p = pa; p < pb; ++p) {
+    const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rank += kp[e] > (4 * p + e < c ? km : key);
+  }
+#pragma unroll 4
+  for (int p = pb; p < p1; ++p) {
+    const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rank += kp[e] > key;
+  }
+  if (P > 1) {
+    if (part > 0 && c < ngt) cnt[(part - 1) * span + c] = rank;   // compaction counts are spent
     __syncthreads();
-    if (!half && c < kk) {
-      rank += cg[c];
-      sel_idx[rank] = j;
-      sel_key[rank] = key;
-    }
-  } else if (tid < kk) {
-    const uint32_t key = cand_key[tid];
-    const int j = cand_idx[tid];
-    const int rank = rank_range(key, j, 0, kk4);
-    sel_idx[rank] = j;
+    if (part == 0 && c < ngt)
+      for (int q = 1; q < P; ++q) rank += cnt[(q - 1) * span + c];
+  }
+  if (part == 0 && c < ngt) {
+    sel_idx[rank] = cand_idx[c];
     sel_key[rank] = key;
   }
   __syncthreads();
   return kk;
 }
+
 
 // ---------------------------------------------------------------- capped eviction
 struct EvictScratch {
@@ -421,7 +452,7 @@ __device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int s
   if (tid < ((K + 1) & ~1) - K) x.vkey[K + tid] = ~0ull;   // pad to an even count
   __syncthreads();
   // rank every eligible key among all K: P threads per candidate, each over
-  // 1/P of the list (all four waves busy), partial counts summed through LDS
+  // 1/P of the list (every wave busy), partial counts summed through LDS
   {
     const int P = K <= kThreads / 4 ? 4 : (K <= kThreads / 2 ? 2 : 1);
     const int span = kThreads / P;

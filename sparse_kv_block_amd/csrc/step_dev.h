@@ -37,7 +37,9 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   const int c0 = n * CPL;
   float Qh[CPL], Ah[CPL];
   group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Qh, Ah);
-  const int Gw = nb > 4 * w ? (nb - 4 * w + 15) / 16 : 0;   // this wave's record groups
+  // record groups: group t of wave w holds records 4*kWaves*t + 4*w + quad
+  constexpr int GS = 4 * kWaves;
+  const int Gw = nb > 4 * w ? (nb - 4 * w + GS - 1) / GS : 0;
 
   // Group loads are issued unconditionally (a group past the end loads a
   // clamped in-range record and is ignored): a branch around a load makes
@@ -46,7 +48,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   auto load_groups = [&](int t, int cnt, Row* lo, Row* hi) {
 #pragma unroll
     for (int k = 0; k < cnt; ++k) {
-      int j = 16 * (t + k) + 4 * w + quad;
+      int j = GS * (t + k) + 4 * w + quad;
       j = (t + k < Gw && j < nb) ? j : (nb > 0 ? nb - 1 : 0);
       const uint16_t* rec = summ_unit + (size_t)j * 2 * D + c0;
       lo[k] = __builtin_nontemporal_load(reinterpret_cast<const Row*>(rec));
@@ -64,7 +66,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
         fh[2 * i] = bf16_lo(hi[k][i]); fh[2 * i + 1] = bf16_hi(hi[k][i]);
       }
       const float s = row16_sum(record_part<CPL>(fl, fh, Qh, Ah));
-      const int j = 16 * (t + k) + 4 * w + quad;
+      const int j = GS * (t + k) + 4 * w + quad;
       if (n == 0 && j < nb) keys[j] = score_key(s);
     }
   };
