@@ -147,6 +147,71 @@ def test_topk_with_more_slots_than_blocks_and_large_context():
     check_topk(i32(layer.topk_idx), host(layer.topk_score), idx, sc, what="large")
 
 
+def designed_scores(nb: int, pattern: int) -> np.ndarray:
+    """Per-block values v_j (all exact in bf16) whose scores G * v_j exercise
+    the top-K's distinct paths: all keys equal (no radix round), one outlier
+    above a cluster, powers of two over ~120 binades (the highest differing
+    bit is the sign/exponent), ties at the threshold, a negative cluster, and
+    distinct integers (the search ends early on an exact digit)."""
+    j = np.arange(nb)
+    if pattern == 0:
+        return np.full(nb, 3.0)
+    if pattern == 1:
+        v = np.ones(nb)
+        v[min(7, nb - 1)] = 200.0
+        return v
+    if pattern == 2:
+        e = (j * 37) % 120 - 60
+        return np.where(j % 3 == 0, -1.0, 1.0) * np.exp2(e.astype(np.float64))
+    if pattern == 3:
+        return (j % 5).astype(np.float64)
+    if pattern == 4:
+        return -(1.0 + (j % 3) / 4.0)
+    return ((j * 101) % 256).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [16, 128])
+def test_topk_designed_key_distributions(dtype, K):
+    # one-hot draft and normal queries on channel 0 make block j's score
+    # G * (its largest channel-0 key), so each unit's scores follow one
+    # designed pattern exactly; the standalone scan + top-K and the fused
+    # step must both reproduce the oracle's order bit for bit
+    cfg = small(dtype=dtype, batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128, k_resident=K,
+                ctx=16000)
+    ctx = np.array([16000, 16000 - 40, 2100], np.int32)
+    nbmax = cfg.max_blocks(int(ctx.max()))
+    B, H, S, d = cfg.batch, cfg.n_kv_heads, cfg.block_size, cfg.head_dim
+    rec = torch.zeros((B, H, nbmax, 2, S, d), dtype=torch.float32)    # V = 0: only the order matters
+    for b in range(B):
+        nb = cfg.max_blocks(int(ctx[b]))
+        for h in range(H):
+            v = torch.from_numpy(designed_scores(nb, (b * H + h) % 6)).to(torch.float32)
+            rec[b, h, :nb, 0, :, 0] = v[:, None]
+        tok = torch.arange(nbmax * S).reshape(nbmax, S)
+        rec[b, :, :, 0] *= (tok < int(ctx[b])).to(torch.float32)[None, :, :, None]
+    dt = gen.TORCH_DTYPE[dtype]
+    rec = rec.reshape(B, H, nbmax, 2 * S * d).to(dt).to(DEV)
+    q = torch.zeros((B, 2, cfg.n_q_heads, d), dtype=torch.float32)
+    q[..., 0] = 1.0
+    q = q.to(dt).to(DEV)
+    say("designed top-K:", dtype, "K", K, "nbmax", nbmax)
+    summ = oracle.summarize(rec.cpu(), ctx, 16)
+    sc = oracle.block_scores(q.cpu(), summ, ctx, 16)
+    idx, val = oracle.topk(sc, ctx, 16, K)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score)
+    np.testing.assert_array_equal(i32(layer.topk_idx), idx)
+    np.testing.assert_array_equal(host(layer.topk_score).astype(np.float64), val)
+    layer.cold_fill(q, rec)
+    layer.topk_idx.fill_(-7)
+    layer.step(q, 1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(i32(layer.topk_idx), idx)
+    np.testing.assert_array_equal(host(layer.topk_score).astype(np.float64), val)
+
+
 # --------------------------------------------------------------------------- eviction
 @pytest.mark.parametrize("seed", range(4))
 @pytest.mark.parametrize("K", [8, 128, 256])
