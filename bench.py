@@ -95,12 +95,12 @@ def cpu_baseline(cfg, ctx, records_host, qs_host, min_cpu_seconds: float):
                       f"eviction) in {spent:.2f} s wall on {nth} threads"}
 
 
-def dense_leg(cfg, layer, rec_host, q, reps: int = 10):
+def dense_leg(cfg, layer, rec, q, reps: int = 10):
     """The dense comparator on the same layer: attention of both rows over the
-    full KV held in HBM (the capacity the method avoids needing)."""
+    full KV held in HBM (`rec`, the device copy of the records; the capacity
+    the method avoids needing)."""
     import torch
     from sparse_kv_block_amd import lib
-    rec = rec_host.to("cuda")
     ws = lib.dense_attn_workspace(layer.shape)
     out = torch.empty_like(layer.out)
     for _ in range(2):
@@ -114,18 +114,16 @@ def dense_leg(cfg, layer, rec_host, q, reps: int = 10):
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
     kv = rec.numel() * rec.element_size()
-    del rec, ws
-    torch.cuda.empty_cache()
     log(f"[bench] dense attention over {kv / 2**30:.1f} GiB of KV: {us:.1f} us, {kv / us / 1e3:.0f} GB/s")
     return {"us": round(us, 2), "kv_bytes": kv, "GBps": round(kv / us / 1e3, 1),
             "hbm_kv_per_layer_GiB": round(kv / 2**30, 2)}
 
 
-def kernels_leg(cfg, layer, ctx, nbmax, qs, reps: int = 10):
+def kernels_leg(cfg, layer, ctx, nbmax, qs, rec, reps: int = 10):
     """Each standalone kernel of the step on the timed layer's state, timed
     with HIP events on the current stream (median of `reps`), against its
-    algorithmic bytes: summarize (reads every key of the full KV, here a
-    device-resident copy), look-ahead attention (the resident pool),
+    algorithmic bytes: summarize (reads every key of the full KV, here the
+    device-resident copy `rec`), look-ahead attention (the resident pool),
     summary scan + top-K (the summaries), capped eviction (maps only)."""
     import torch
     from sparse_kv_block_amd import gen, lib
@@ -150,14 +148,14 @@ def kernels_leg(cfg, layer, ctx, nbmax, qs, reps: int = 10):
             ts.append(a.elapsed_time(b) * 1e3)
         return float(np.median(ts))
 
+    torch.cuda.synchronize()
+    time.sleep(1.0)                 # earlier legs may have freed large buffers
     out = {}
-    rec = gen.records(cfg, ctx, nbmax, device=layer.device)
     summ = torch.empty_like(layer.summ)
     us = timed(lambda: lib.summarize(sh, rec, layer.ctx_len, summ))
     byt = sum_blocks * (16 * cfg.head_dim * es + 2 * cfg.head_dim * es)
     out["summarize"] = {"us": round(us, 1), "bytes": byt, "GBps": round(byt / us / 1e3, 1)}
-    del rec, summ
-    torch.cuda.empty_cache()
+    del summ
     q = qs[0]
     us = timed(lambda: lib.lookahead_attn(sh, q, layer.pool, layer.p2l, layer.ctx_len, layer.out))
     byt = units * cfg.k_resident * 2 * 16 * cfg.head_dim * es + 2 * q.numel() * es
@@ -429,8 +427,8 @@ def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", default="qwen3_8b_16k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time (wall x threads) the oracle baseline runs for")
@@ -487,18 +485,23 @@ def main():
         f"in {time.perf_counter() - t0:.1f} s")
     layer = Layer(cfg, ctx, nbmax, device=dev)
     layer.summarize(rec_dev)
+    # The host pool (pinned) feeds the cold fill and the prefetch; the device
+    # copy stays allocated for the dense and per-kernel legs.  Freeing it
+    # before the timed steps left the driver clearing the freed memory in the
+    # background, which took HBM bandwidth from the first second of timed
+    # work (measured 258 instead of 250 us per step).
     rec_host = torch.empty(rec_dev.shape, dtype=rec_dev.dtype, pin_memory=True)
     rec_host.copy_(rec_dev)
-    del rec_dev
     torch.cuda.synchronize()
-    torch.cuda.empty_cache()
     layer.cold_fill(qs[0], rec_host)
     torch.cuda.synchronize()
     log("[bench] cold fill done")
     dense = None
     if args.dense:
-        dense = dense_leg(cfg, layer, rec_host, qs[0])
+        dense = dense_leg(cfg, layer, rec_dev, qs[0])
 
+    # Warm-up: after idle the first ~5 ms of steps run a few per cent slower
+    # (clock ramp), hence the 200-step default.
     stream = torch.cuda.current_stream()
     step = 0
     for _ in range(args.warmup):
@@ -506,19 +509,31 @@ def main():
         layer.step(qs[(step - 1) % nq], step)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: two events on the kernel's stream bracket the K launches
+    # (an event pair around every launch would put a marker between every two
+    # launches, a ~10 us gap each); their span over K is the average launch
+    # duration.  The per-launch spread comes from a separate pass afterwards.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
         step += 1
-        starts[i].record(stream)
         layer.step(qs[(step - 1) % nq], step)
-        ends[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_kernel_s = float(np.mean(kern_ms)) / 1e3
+    avg_kernel_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    spread = []
+    for _ in range(20):
+        step += 1
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        layer.step(qs[(step - 1) % nq], step)
+        b.record(stream)
+        spread.append((a, b))
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in spread]
     median_kernel_us = float(np.median(kern_ms)) * 1e3
     ms_per_step = wall / args.steps * 1e3
     value = args.steps / wall
@@ -526,7 +541,8 @@ def main():
     achieved = algo["total"] / avg_kernel_s / 1e9
     admits = int(layer.admit_count.sum().item())
     log(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms: {value:.1f} layer-steps/s; kernel avg "
-        f"{avg_kernel_s * 1e6:.1f} us (min {min(kern_ms) * 1e3:.1f}), {achieved:.0f} GB/s; "
+        f"{avg_kernel_s * 1e6:.1f} us, {achieved:.0f} GB/s (per launch: min {min(kern_ms) * 1e3:.1f}, "
+        f"median {median_kernel_us:.1f} us); "
         f"last step admitted {admits} blocks")
 
     result = {
@@ -592,7 +608,7 @@ def main():
         result["pipeline_36_layer"] = pipeline_leg(layer, rec_host, args.pipeline_steps, 2)
 
     if args.kernels:
-        result["per_kernel"] = kernels_leg(cfg, layer, ctx, nbmax, qs)
+        result["per_kernel"] = kernels_leg(cfg, layer, ctx, nbmax, qs, rec_dev)
     if args.capmodel:
         if "pcie" not in result:
             log("[bench] --capmodel needs the prefetch leg (drop --no-pcie)")
