@@ -42,24 +42,34 @@ __host__ __device__ constexpr int attn_lds_bytes(int D, int RT) {
 // TW = row tiles one wave holds.  TW == RT == 2: every wave takes both tiles
 // of its quarter of the slots (each record fetched once per workgroup, twice
 // the accumulators per wave).
-template <int D, int RT, int TW = 1>
+//
+// QL: the query operands, identical in every wave when TW == RT, live once
+// per workgroup in LDS (TW * KS * 64 16-byte entries at `qlds`, written by
+// wave 0 in init(); the caller puts a barrier between init() and the first
+// process()) and each logit MFMA reads its operand from there: 8 * TW VGPRs
+// per lane fewer for the same arithmetic.
+template <int D, int RT, int TW = 1, bool QL = false>
 struct AttnWave {
   static constexpr int KS = D / 32;   // logit MFMA steps
   static constexpr int NT = D / 16;   // output tiles
   static constexpr int REC = 2 * kBlock * D;
   static constexpr bool kPairs = RT == 2 && TW == 1;   // waves paired on a slot half
   static constexpr int NSPLIT = kPairs ? kWaves / 2 : kWaves;
+  static_assert(!QL || TW == RT, "LDS query operands need every wave to hold every tile");
+  static constexpr int QLDS_BYTES = QL ? TW * KS * kWave * 16 : 0;
 
   int w, g, n, rt, split;
-  bf16x8 qop[TW][KS];
+  bf16x8 qop[QL ? 1 : TW][QL ? 1 : KS];
+  const bf16x8* qlds;
   float m_run[TW], l_run[TW];
   f32x4 acc[TW][NT];
   const uint16_t* unit_pool;
 
   // unit_base: the unit's first record (slot 0 of its pool, or block 0 of its
-  // records for the dense variant).
+  // records for the dense variant).  q_area: QLDS_BYTES of LDS (QL only).
   __device__ __forceinline__ void init(const Shape& sh, const uint16_t* __restrict__ q,
-                                       const uint16_t* __restrict__ unit_base, int b, int h) {
+                                       const uint16_t* __restrict__ unit_base, int b, int h,
+                                       void* q_area = nullptr) {
     const int lane = threadIdx.x % kWave;
     w = threadIdx.x / kWave;
     g = lane >> 4;
@@ -77,11 +87,17 @@ struct AttnWave {
       const uint16_t* qr = q + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
+        bf16x8 v;
         if (valid) {
-          qop[t][kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
+          v = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
         } else {
           u32x4 z = {0u, 0u, 0u, 0u};
-          qop[t][kk] = __builtin_bit_cast(bf16x8, z);
+          v = __builtin_bit_cast(bf16x8, z);
+        }
+        if constexpr (QL) {
+          if (w == 0) static_cast<bf16x8*>(q_area)[(t * KS + kk) * kWave + lane] = v;
+        } else {
+          qop[t][kk] = v;
         }
       }
       m_run[t] = -INFINITY;
@@ -90,6 +106,7 @@ struct AttnWave {
       for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     unit_pool = unit_base;
+    qlds = static_cast<const bf16x8*>(q_area);
   }
 
   // This wave's slots are split, split + NSPLIT, split + 2*NSPLIT, ...: the
@@ -135,8 +152,12 @@ struct AttnWave {
     for (int t = 0; t < TW; ++t) {
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qop[t][kk], z, 0, 0, 0);
+      for (int kk = 0; kk < KS; ++kk) {
+        bf16x8 qv;
+        if constexpr (QL) qv = qlds[(t * KS + kk) * kWave + g * 16 + n];
+        else qv = qop[t][kk];
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qv, z, 0, 0, 0);
+      }
       float zz[4];
       float bm = -INFINITY;
 #pragma unroll

@@ -422,11 +422,11 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     if (part == 0) attention();
     else kk = scan_select();
   } else if (IL && kMfma) {
-    // one pass streams the unit's blocks and its summary records together
-    // (one summary group per block step with 32 rows: two would not fit
-    // 2 waves per SIMD)
+    // one pass streams the unit's blocks and its summary records together,
+    // two summary groups per block step (with 32 rows the query operands sit
+    // in LDS so that both groups fit 2 waves per SIMD)
     if constexpr (IL && kMfma) {
-      attn_scan_unit_bf16<D, RT, (RT == 1 ? 2 : 1), 8, RT>(
+      attn_scan_unit_bf16<D, RT, 2, 8, RT, (RT == 2)>(
           sh, q, pool, p2l, summ + (size_t)unit * sh.NBmax * 2 * D, nb, b, h, L, scale, out,
           reinterpret_cast<float*>(smem), p.keys);
       __syncthreads();

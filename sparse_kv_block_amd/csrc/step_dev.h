@@ -19,7 +19,7 @@ namespace oasis {
 // Requires at most 64 slots per wave (K <= 256 with one row tile, K <= 128
 // with two).  Writes keys[j] for j < nb and the attention output; ends with the attention merge (so the keys are complete in LDS for
 // the whole workgroup afterwards).
-template <int D, int RT, int SG, int UL, int TW = RT>
+template <int D, int RT, int SG, int UL, int TW = RT, bool QL = false>
 __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ pool,
                                                     const int32_t* __restrict__ p2l,
@@ -27,12 +27,15 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
                                                     int b, int h, int L, float scale_log2,
                                                     uint16_t* __restrict__ out, float* lds,
                                                     uint32_t* keys) {
-  using AW = AttnWave<D, RT, TW>;
+  using AW = AttnWave<D, RT, TW, QL>;
   constexpr int CPL = D / 16;
   constexpr int RW = CPL / 2;          // 32-bit words of one summary row slice
   AW a;
   const int unit = b * sh.H + h;
-  a.init(sh, q, pool + (size_t)unit * sh.K * AW::REC, b, h);
+  // with QL the query operands go to the start of the merge area, which the
+  // merge first writes after its own first barrier
+  a.init(sh, q, pool + (size_t)unit * sh.K * AW::REC, b, h, lds);
+  if constexpr (QL) __syncthreads();
   const int w = a.w, quad = a.g, n = a.n;
   const int c0 = n * CPL;
   float Qh[CPL], Ah[CPL];
