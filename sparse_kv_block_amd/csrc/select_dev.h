@@ -406,15 +406,16 @@ __device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int s
                                            const EvictScratch& x) {
   const int tid = threadIdx.x;
   const int w = tid / kWave;
+  // the slot lookups of T and the unit's slot map go out in one round trip
+  const int j = tid < K ? T[tid] : -1;
+  const bool valid = j >= 0 && j < NBmax;
+  const int s = valid ? l2p[j] : -1;
   if (tid < K) {
     x.p2l_s[tid] = p2l[tid];
     x.ls_s[tid] = ls[tid];
   }
   __syncthreads();
   // 1. stamp resident members of T; flag the missing ones
-  const int j = tid < K ? T[tid] : -1;
-  const bool valid = j >= 0 && j < NBmax;
-  const int s = valid ? l2p[j] : -1;
   const bool hit = valid && s >= 0 && s < K;
   const bool miss = valid && !hit;
   if (hit) x.ls_s[s] = step;

@@ -107,6 +107,7 @@ def main():
     s.add_argument("dir")
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--top", type=int, default=12)
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -119,7 +120,7 @@ def main():
     c.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.what == "stats":
-        print(stats(a.dir, a.cmd, a.out))
+        print(stats(a.dir, a.cmd, a.out, a.top))
     else:
         print(json.dumps(counters(a.fetch, a.write, a.kernel, a.copy_kernel, a.copy_bytes,
                                   a.cmd_fetch, a.cmd_write, a.out, a.algorithmic_bytes), indent=1))
