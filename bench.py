@@ -457,7 +457,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the look-ahead step has "
-              "no cross-GPU exchange, see the sharding notes in DESIGN.md", file=sys.stderr)
+              "no cross-GPU exchange: every (request, KV head) unit is independent, so requests or "
+              "KV heads shard across GPUs with no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch
