@@ -4,10 +4,17 @@
     python -m sparse_kv_block_amd.profiling counters --fetch DIR1 --write DIR2 \
         --kernel layer_step_bf16 --copy-kernel elementwise --copy-bytes N \
         --cmd-fetch "..." --cmd-write "..." --out profiles/X.json
+    python -m sparse_kv_block_amd.profiling per-kernel --fetch DIR1 --write DIR2 \
+        --stats DIR3 --copy-kernel elementwise --copy-bytes N \
+        --cmd-fetch "..." --cmd-write "..." --cmd-stats "..." --out profiles/X.md
 
 `counters` scales the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
 what the same counters read for a plain copy kernel of known size, and records
 a hash of the HIP sources so that stale numbers can be recognised.
+`per-kernel` does the same for every kernel of the library that the runs
+launched and divides the bytes by the kernel's median duration from a
+separate kernel-trace run (counter runs serialise dispatches, so their own
+timestamps are not used), as a table of HBM GB/s per kernel.
 """
 from __future__ import annotations
 
@@ -100,6 +107,49 @@ def counters(fetch_dir, write_dir, kernel, copy_kernel, copy_bytes, cmd_fetch, c
     return rec
 
 
+def _short(name: str) -> str:
+    n = name.split("(")[0]
+    return n[5:] if n.startswith("void ") else n
+
+
+def per_kernel(fetch_dir, write_dir, stats_dir, copy_kernel, copy_bytes, cmds, out,
+               match="oasis::", peak_gbs=8000.0):
+    f_c, _ = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", copy_kernel)
+    w_c, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", copy_kernel)
+    sf = copy_bytes / (f_c * 1024.0)
+    sw = copy_bytes / (w_c * 1024.0)
+    names = sorted({r["Kernel_Name"] for r in _rows(_find(fetch_dir, "counter_collection.csv"))
+                    if match in r["Kernel_Name"]})
+    spans = {}
+    for r in _rows(_find(stats_dir, "kernel_trace.csv")):
+        spans.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# HBM traffic per kernel (rocprofv3 counters)", "",
+             f"Kernel sources: {kernel_source_hash()}.",
+             f"FETCH_SIZE x {sf:.4f} and WRITE_SIZE x {sw:.4f} give bytes: the factors make a "
+             f"plain {copy_bytes} B copy kernel ({copy_kernel}) read and write {copy_bytes} B.",
+             "Bytes: median over a kernel's dispatches in the counter runs. Durations: median "
+             "over its dispatches in the kernel-trace run. GB/s = (read + write) / duration; "
+             f"% of the {peak_gbs:.0f} GB/s HBM peak (the gather and append kernels move "
+             "their bytes over the host link, not HBM).", "",
+             "| kernel | dispatches | read MB | write MB | median us | GB/s | % peak |",
+             "|---|---|---|---|---|---|---|"]
+    for name in names:
+        fk, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", name)
+        wk, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", name)
+        rb, wb = fk * 1024.0 * sf, wk * 1024.0 * sw
+        sp = spans.get(name)
+        us = statistics.median(sp) if sp else float("nan")
+        gbs = (rb + wb) / us / 1e3 if sp else float("nan")
+        lines.append(f"| `{_short(name)}` | {nf} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {us:.1f} | "
+                     f"{gbs:.0f} | {100 * gbs / peak_gbs:.0f} |")
+    lines += ["", "Commands:", ""] + [f"    {c}" for c in cmds]
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -118,7 +168,21 @@ def main():
     c.add_argument("--cmd-write", required=True)
     c.add_argument("--algorithmic-bytes", type=int, default=None)
     c.add_argument("--out", required=True)
+    k = sub.add_parser("per-kernel")
+    k.add_argument("--fetch", required=True)
+    k.add_argument("--write", required=True)
+    k.add_argument("--stats", required=True)
+    k.add_argument("--copy-kernel", required=True)
+    k.add_argument("--copy-bytes", type=int, required=True)
+    k.add_argument("--cmd-fetch", required=True)
+    k.add_argument("--cmd-write", required=True)
+    k.add_argument("--cmd-stats", required=True)
+    k.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.what == "per-kernel":
+        print(per_kernel(a.fetch, a.write, a.stats, a.copy_kernel, a.copy_bytes,
+                         [a.cmd_stats, a.cmd_fetch, a.cmd_write], a.out))
+        return
     if a.what == "stats":
         print(stats(a.dir, a.cmd, a.out, a.top))
     else:
