@@ -167,20 +167,29 @@ struct AttnWave {
       }
       bm = xrow_max(bm);
       // f is 1 unless the block max exceeds the running max by more than 8;
-      // multiplying unconditionally keeps the accumulators in place.
+      // the rescale runs only when some row of the wave needs it (rows that
+      // do not multiply by 1).
       const bool need = bm > m_run[t] + 8.0f;
       const float f = need ? exp2f(m_run[t] - bm) : 1.0f;
       m_run[t] = need ? bm : m_run[t];
-      l_run[t] *= f;
+      if (ballot(need)) {
+        l_run[t] *= f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[t][nt] *= f;
-      i16x4 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t hb = f32_to_bf16_bits(exp2f(zz[i] - m_run[t]));
-        pb[i] = (short)hb;
-        l_run[t] += bf16_bits_to_f32(hb);
+        for (int nt = 0; nt < NT; ++nt) acc[t][nt] *= f;
       }
+      // weights rounded to bf16 (round to nearest even, v_cvt_pk_bf16_f32)
+      // for the P.V product; the denominator sums the rounded weights
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = exp2f(zz[i] - m_run[t]);
+      const bf16x2 p01 = __builtin_convertvector((f32x2){e[0], e[1]}, bf16x2);
+      const bf16x2 p23 = __builtin_convertvector((f32x2){e[2], e[3]}, bf16x2);
+      l_run[t] += (float)p01[0];
+      l_run[t] += (float)p01[1];
+      l_run[t] += (float)p23[0];
+      l_run[t] += (float)p23[1];
+      const u32x2 pw = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+      const i16x4 pb = __builtin_bit_cast(i16x4, pw);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt], pb, acc[t][nt], 0, 0, 0);

@@ -17,6 +17,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct Shape {
   int B, Hq, H, G, d, NBmax, K;
@@ -86,15 +88,41 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // Max / sum over lanes l, l^16, l^32, l^48 (the four lanes that share l % 16).
+// Lane l's value beside that of lane l ^ 16 (l ^ 32): v_permlane16_swap
+// (v_permlane32_swap) on two copies of x leaves the two values of every lane
+// pair in (a, b) in both lanes, as VALU moves with no LDS round trip.
+__device__ __forceinline__ void xor16_pair(float x, float& a, float& b) {
+  const u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void xor32_pair(float x, float& a, float& b) {
+  const u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the same lane of the four
+// 16-lane rows); min, max and the two-operand sums are commutative, so the
+// result is the same in all four lanes.
 __device__ __forceinline__ float xrow_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  float a, b;
+  xor16_pair(x, a, b);
+  xor32_pair(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xrow_min(float x) {
+  float a, b;
+  xor16_pair(x, a, b);
+  xor32_pair(fminf(a, b), a, b);
+  return fminf(a, b);
 }
 __device__ __forceinline__ float xrow_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  float a, b;
+  xor16_pair(x, a, b);
+  xor32_pair(a + b, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ float wave_max(float x) {

@@ -56,10 +56,8 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(Shape sh, const T* 
   }
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    mn[c] = fminf(mn[c], __shfl_xor(mn[c], 16));
-    mn[c] = fminf(mn[c], __shfl_xor(mn[c], 32));
-    mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 16));
-    mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 32));
+    mn[c] = xrow_min(mn[c]);
+    mx[c] = xrow_max(mx[c]);
   }
   if (g == 0) {
     T* out = summ + ((size_t)unit * sh.NBmax + j) * 2 * D + c0;
