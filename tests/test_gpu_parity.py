@@ -66,6 +66,9 @@ SMALL_CASES = [
     dict(dtype="bf16", head_dim=64, n_q_heads=4, n_kv_heads=4),
     dict(dtype="bf16", head_dim=128, n_q_heads=32, n_kv_heads=2, k_resident=24),     # G = 16
     dict(dtype="f32", head_dim=128, n_q_heads=6, n_kv_heads=2, k_resident=40),
+    # 24 stacked rows: the second 16-row tile is partly empty
+    dict(dtype="bf16", head_dim=64, n_q_heads=24, n_kv_heads=2, k_resident=16),
+    dict(dtype="bf16", head_dim=128, n_q_heads=12, n_kv_heads=1, k_resident=32, batch=2),
 ]
 RAGGED = [1000, 17, 0]      # partial last block, one full block + 1 token, empty request
 
@@ -322,13 +325,17 @@ def test_fused_step_equals_separate_calls(case):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
 
 
-@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 128), ("bf16", 256)])
-def test_fused_step_split_scan_equals_separate_calls(dtype, K):
+@pytest.mark.parametrize("dtype,K,hq,hkv,d", [("bf16", 128, 8, 2, 128), ("f32", 128, 8, 2, 128),
+                                              ("bf16", 256, 8, 2, 128), ("bf16", 128, 32, 2, 128),
+                                              ("bf16", 64, 8, 2, 64)])
+def test_fused_step_split_scan_equals_separate_calls(dtype, K, hq, hkv, d):
     # contexts past 1024 blocks split the scan over several workgroups whose
     # lists a second launch merges; the result must equal one workgroup's
     # (separate calls)
-    # K = 256 at 8192 blocks: the merge sees its largest input, 8 lists of 256
-    cfg = small(dtype=dtype, batch=4, k_resident=K, n_q_heads=8, n_kv_heads=2, planted=0)
+    # K = 256 at 8192 blocks: the merge sees its largest input, 8 lists of 256;
+    # 32 query heads per 2 KV heads: two row tiles; d = 64
+    cfg = small(dtype=dtype, batch=4, k_resident=K, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                planted=0)
     ctx = [131072, 40000, 16 * 1024 + 1, 900]
     ctx, nbmax, rec, q = setup(cfg, ctx, seed=12)
     assert lib.layer_step_workspace_bytes(lib.Shape.of(cfg, nbmax)) > 0
