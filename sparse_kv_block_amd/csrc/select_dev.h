@@ -5,9 +5,9 @@
 // scans per-block min/max key summaries and ranks every logical block per KV
 // head).  The group score of block j is
 //     sum_i sum_c max(q_ic * min_jc, q_ic * max_jc),
-// which for min <= max equals sum_c [(min+max)/2 * Q_c + (max-min)/2 * A_c]
-// with Q_c = sum_i q_ic and A_c = sum_i |q_ic|: two FMAs per channel per block
-// instead of 2G.  Sixteen lanes share one 512-byte bf16 summary record (8
+// which for min <= max equals sum_c [min_jc * N_c + max_jc * P_c] with
+// N_c = sum_i min(q_ic, 0) and P_c = sum_i max(q_ic, 0): two FMAs per channel
+// per block instead of 2G.  Sixteen lanes share one 512-byte bf16 summary record (8
 // channels each, one 16-byte load of the min row and one of the max row) and
 // reduce with DPP inside their 16-lane row; a wave covers 4 blocks per load.
 // Summary loads are nontemporal (read once per step).  The scores of the
@@ -99,34 +99,34 @@ struct Raw {
   }
 };
 
-// Halved group sums of the query row over the G query heads of KV head h, for
-// channels c0 .. c0+CPL: Qh = sum_i q_ic / 2, Ah = sum_i |q_ic| / 2.
+// Sign-split group sums of the query row over the G query heads of KV head h,
+// for channels c0 .. c0+CPL: Nq = sum_i min(q_ic, 0), Pq = sum_i max(q_ic, 0).
+// With min_c <= max_c, max(q min_c, q max_c) = min(q, 0) min_c + max(q, 0) max_c,
+// so the group's summed Quest bound is sum_c (Nq_c min_c + Pq_c max_c).
 template <typename T, int D, int CPL>
 __device__ __forceinline__ void group_query_sums(const Shape& sh, const T* __restrict__ q,
-                                                 int q_row, int b, int h, int c0, float* Qh,
-                                                 float* Ah) {
+                                                 int q_row, int b, int h, int c0, float* Nq,
+                                                 float* Pq) {
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) { Qh[i] = 0.f; Ah[i] = 0.f; }
+  for (int i = 0; i < CPL; ++i) { Nq[i] = 0.f; Pq[i] = 0.f; }
   for (int i = 0; i < sh.G; ++i) {
     float v[CPL];
     Elem<T>::template load<CPL>(q + ((size_t)(b * 2 + q_row) * sh.Hq + h * sh.G + i) * D + c0, v);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) { Qh[c] += v[c]; Ah[c] += fabsf(v[c]); }
+    for (int c = 0; c < CPL; ++c) { Nq[c] += fminf(v[c], 0.f); Pq[c] += fmaxf(v[c], 0.f); }
   }
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) { Qh[c] *= 0.5f; Ah[c] *= 0.5f; }
 }
 
 // This lane's part of one block's score (channels of its slice), in the
 // channel order every scan path uses, so all of them agree bit for bit.
 template <int CPL>
-__device__ __forceinline__ float record_part(const float* lo, const float* hi, const float* Qh,
-                                             const float* Ah) {
+__device__ __forceinline__ float record_part(const float* lo, const float* hi, const float* Nq,
+                                             const float* Pq) {
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    s = fmaf(lo[c] + hi[c], Qh[c], s);
-    s = fmaf(hi[c] - lo[c], Ah[c], s);
+    s = fmaf(lo[c], Nq[c], s);
+    s = fmaf(hi[c], Pq[c], s);
   }
   return s;
 }
@@ -146,8 +146,8 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
   const int n = lane & 15;
   const int c0 = n * CPL;
 
-  float Qh[CPL], Ah[CPL];
-  group_query_sums<T, D, CPL>(sh, q, q_row, b, h, c0, Qh, Ah);
+  float Nq[CPL], Pq[CPL];
+  group_query_sums<T, D, CPL>(sh, q, q_row, b, h, c0, Nq, Pq);
 
   const T* last = summ_unit + (size_t)(nb > 0 ? nb - 1 : 0) * 2 * D + c0;
   for (int jb = w * 4; jb < nb; jb += kThreads / 16 * U) {
@@ -164,7 +164,7 @@ __device__ __forceinline__ void scan_unit(const Shape& sh, const T* __restrict__
       float fl[CPL], fh[CPL];
       lo[u].unpack(fl);
       hi[u].unpack(fh);
-      const float s = row16_sum(record_part<CPL>(fl, fh, Qh, Ah));
+      const float s = row16_sum(record_part<CPL>(fl, fh, Nq, Pq));
       const int j = jb + quad + (kThreads / 16) * u;
       if (n == 0 && j < nb) keys[j] = score_key(s);
     }

@@ -38,8 +38,8 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   if constexpr (QL) __syncthreads();
   const int w = a.w, quad = a.g, n = a.n;
   const int c0 = n * CPL;
-  float Qh[CPL], Ah[CPL];
-  group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Qh, Ah);
+  float Nq[CPL], Pq[CPL];
+  group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Nq, Pq);
   // record groups: group t of wave w holds records 4*kWaves*t + 4*w + quad
   constexpr int GS = 4 * kWaves;
   const int Gw = nb > 4 * w ? (nb - 4 * w + GS - 1) / GS : 0;
@@ -68,7 +68,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
         fl[2 * i] = bf16_lo(lo[k][i]); fl[2 * i + 1] = bf16_hi(lo[k][i]);
         fh[2 * i] = bf16_lo(hi[k][i]); fh[2 * i + 1] = bf16_hi(hi[k][i]);
       }
-      const float s = row16_sum(record_part<CPL>(fl, fh, Qh, Ah));
+      const float s = row16_sum(record_part<CPL>(fl, fh, Nq, Pq));
       const int j = GS * (t + k) + 4 * w + quad;
       if (n == 0 && j < nb) keys[j] = score_key(s);
     }
