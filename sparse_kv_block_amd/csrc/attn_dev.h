@@ -170,7 +170,7 @@ struct AttnWave {
       // the rescale runs only when some row of the wave needs it (rows that
       // do not multiply by 1).
       const bool need = bm > m_run[t] + 8.0f;
-      const float f = need ? exp2f(m_run[t] - bm) : 1.0f;
+      const float f = need ? __builtin_amdgcn_exp2f(m_run[t] - bm) : 1.0f;
       m_run[t] = need ? bm : m_run[t];
       if (ballot(need)) {
         l_run[t] *= f;
@@ -178,10 +178,12 @@ struct AttnWave {
         for (int nt = 0; nt < NT; ++nt) acc[t][nt] *= f;
       }
       // weights rounded to bf16 (round to nearest even, v_cvt_pk_bf16_f32)
-      // for the P.V product; the denominator sums the rounded weights
+      // for the P.V product; the denominator sums the rounded weights.  The
+      // bare v_exp_f32: a weight below 2^-126 of the running maximum comes
+      // out as 0 instead of a denormal
       float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = exp2f(zz[i] - m_run[t]);
+      for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(zz[i] - m_run[t]);
       const bf16x2 p01 = __builtin_convertvector((f32x2){e[0], e[1]}, bf16x2);
       const bf16x2 p23 = __builtin_convertvector((f32x2){e[2], e[3]}, bf16x2);
       l_run[t] += (float)p01[0];
