@@ -123,6 +123,32 @@ def test_score_upper_bounds_every_token_logit(ora, G):
             assert np.all(np.isneginf(sc[b, h, nb:]))
 
 
+def test_sign_split_factoring_of_the_group_bound_equals_the_definition(ora):
+    # The HIP scan factors the group bound per channel as
+    # min_c * sum_i min(q_ic, 0) + max_c * sum_i max(q_ic, 0) (valid for
+    # min_c <= max_c); in fp64 that must reproduce the oracle's definition
+    # sum_i sum_c max(q_ic min_c, q_ic max_c) on real summaries, including
+    # zero query rows and a partial last block.
+    cfg = tiny(n_q_heads=8, n_kv_heads=2, head_dim=16, ctx=203, batch=2)
+    ctx, nbmax, rec, q = make(cfg, seed=21)
+    q = q.clone()
+    q[0, 1, :3] = 0.0                                          # some zero query rows
+    qd = f64(q)
+    summ = ora.summarize(rec, ctx, cfg.block_size)
+    sc = ora.block_scores(q, summ, ctx, cfg.block_size, q_row=1)
+    sm = f64(summ)                                             # [B][H][NB][2][d]
+    G = cfg.group
+    for b in range(cfg.batch):
+        nb = -(-int(ctx[b]) // cfg.block_size)
+        for h in range(cfg.n_kv_heads):
+            qg = qd[b, 1, h * G:(h + 1) * G]                  # [G][d]
+            neg, pos = np.minimum(qg, 0).sum(axis=0), np.maximum(qg, 0).sum(axis=0)
+            mn, mx = sm[b, h, :nb, 0], sm[b, h, :nb, 1]
+            assert np.all(mn <= mx)
+            fact = mn @ neg + mx @ pos
+            np.testing.assert_allclose(fact, sc[b, h, :nb], rtol=1e-12, atol=1e-12)
+
+
 def test_score_with_one_token_blocks_is_the_dot_product(ora):
     # With S = 1 the summary min and max both equal the key, so the bound is
     # exact: score(j) = sum_i q_i . k_j (grouped query heads of the KV head).
