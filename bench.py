@@ -127,6 +127,32 @@ def dense_leg(cfg, layer, rec, q, reps: int = 10):
             "hbm_kv_per_layer_GiB": round(kv / 2**30, 2)}
 
 
+def achievable_leg(mib: int, reps: int = 10) -> dict:
+    """What a plain streaming kernel reaches on this GPU, beside the step: a
+    device-to-device copy of `mib` MiB (the runtime's copy kernel; it reads and
+    writes the bytes once each), timed with HIP events, median of `reps`."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    s = float(np.median(ts))
+    moved = 2 * n * 4
+    del src, dst
+    log(f"[bench] achievable: {mib} MiB device copy {moved / s / 1e9:.0f} GB/s (read + write)")
+    return {"copy_GBps": round(moved / s / 1e9, 1), "copy_bytes": moved,
+            "kind": f"device-to-device copy of {mib} MiB (bytes read + written per second)"}
+
+
 def kernels_leg(cfg, layer, ctx, nbmax, qs, rec, reps: int = 10):
     """Each standalone kernel of the step on the timed layer's state, timed
     with HIP events on the current stream (median of `reps`), against its
@@ -461,6 +487,8 @@ def main():
                     help="also run the top-K agreement study (after every other GPU leg; "
                          "releases the timed layer's buffers)")
     ap.add_argument("--agreement-steps", type=int, default=16)
+    ap.add_argument("--copy-probe-mib", type=int, default=1024,
+                    help="size of the device copy reported as 'achievable'")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, launch a plain elementwise copy of this many MiB "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -587,6 +615,7 @@ def main():
                      "avg_kernel_us": round(avg_kernel_s * 1e6, 2),
                      "median_kernel_us": round(median_kernel_us, 2)},
     }
+    result["achievable"] = achievable_leg(args.copy_probe_mib)
 
     if not args.no_pcie:
         # prefetch leg: the blocks the last step admitted, gather kernel reading

@@ -60,5 +60,6 @@ def test_bench_prints_one_json_line_with_roofline_and_oracle_baseline():
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert 0 < rf["frac"] < 1
+    assert d["achievable"]["copy_GBps"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
