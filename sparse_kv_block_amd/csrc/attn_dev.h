@@ -118,6 +118,24 @@ struct AttnWave {
   }
   __device__ __forceinline__ int slot_of(int i) const { return split + NSPLIT * i; }
 
+  // Logical block held by this wave's slot number ib + lane, loaded
+  // unconditionally (lanes past ie read a clamped slot; tokens_of ignores
+  // them), so that the load can be issued long before its use.
+  __device__ __forceinline__ int slot_block_raw(const Shape& sh, const int32_t* __restrict__ p2l,
+                                                int unit, int ib, int ie) const {
+    const int lane = threadIdx.x % kWave;
+    int k = ib + lane < ie ? ib + lane : ie - 1;
+    k = k < 0 ? 0 : k;
+    return p2l[(size_t)unit * sh.K + slot_of(k)];
+  }
+  // Valid-token count of the slot whose raw block is j (lanes past ie give 0).
+  __device__ __forceinline__ int tokens_of(int j, const Shape& sh, int L, int ib, int ie) const {
+    const int lane = threadIdx.x % kWave;
+    if (lane >= ie - ib || j < 0 || j >= sh.NBmax) return 0;
+    const int nv = L - j * kBlock;
+    return nv < 0 ? 0 : (nv > kBlock ? kBlock : nv);
+  }
+
   // Valid-token count of this wave's slot number ib + lane (lanes past ie give 0).
   __device__ __forceinline__ int slot_tokens(const Shape& sh, const int32_t* __restrict__ p2l, int unit,
                                              int L, int ib, int ie) const {

@@ -109,11 +109,26 @@ __device__ __forceinline__ void group_query_sums(const Shape& sh, const T* __res
                                                  float* Pq) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i) { Nq[i] = 0.f; Pq[i] = 0.f; }
-  for (int i = 0; i < sh.G; ++i) {
-    float v[CPL];
-    Elem<T>::template load<CPL>(q + ((size_t)(b * 2 + q_row) * sh.Hq + h * sh.G + i) * D + c0, v);
+  // four query heads' loads in flight at a time (a load-then-add loop waits a
+  // full round trip per head), summed in head order
+  constexpr int kB = 4;
+  const T* q0 = q + ((size_t)(b * 2 + q_row) * sh.Hq + h * sh.G) * D + c0;
+  for (int i0 = 0; i0 < sh.G; i0 += kB) {
+    float v[kB][CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) { Nq[c] += fminf(v[c], 0.f); Pq[c] += fmaxf(v[c], 0.f); }
+    for (int k = 0; k < kB; ++k) {
+      const int i = i0 + k < sh.G ? i0 + k : sh.G - 1;    // clamped, ignored past G
+      Elem<T>::template load<CPL>(q0 + (size_t)i * D, v[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const bool in = i0 + k < sh.G;    // a select, not a branch: the loads stay together
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        Nq[c] = in ? Nq[c] + fminf(v[k][c], 0.f) : Nq[c];
+        Pq[c] = in ? Pq[c] + fmaxf(v[k][c], 0.f) : Pq[c];
+      }
+    }
   }
 }
 

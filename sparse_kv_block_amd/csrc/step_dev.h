@@ -35,11 +35,15 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   // with QL the query operands go to the start of the merge area, which the
   // merge first writes after its own first barrier
   a.init(sh, q, pool + (size_t)unit * sh.K * AW::REC, b, h, lds);
-  if constexpr (QL) __syncthreads();
+  // the slot map, the query operands and the query sums are loaded together
+  // before the first use of any of them
+  const int ns = a.n_slots(sh);
+  const int j_raw = a.slot_block_raw(sh, p2l, unit, 0, ns);
   const int w = a.w, quad = a.g, n = a.n;
   const int c0 = n * CPL;
   float Nq[CPL], Pq[CPL];
   group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Nq, Pq);
+  if constexpr (QL) __syncthreads();
   // record groups: group t of wave w holds records 4*kWaves*t + 4*w + quad
   constexpr int GS = 4 * kWaves;
   const int Gw = nb > 4 * w ? (nb - 4 * w + GS - 1) / GS : 0;
@@ -75,7 +79,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   };
 
   // ---- interleaved steps: one block + SG record groups each ----
-  const int nv_l = a.slot_tokens(sh, p2l, unit, L, 0, a.n_slots(sh));
+  const int nv_l = a.tokens_of(j_raw, sh, L, 0, ns);
   uint64_t todo = ballot(nv_l > 0);
   auto pop = [&]() -> int {
     if (!todo) return -1;
