@@ -391,6 +391,37 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   const int unit = blockIdx.x % units;
   const int part = blockIdx.x / units;
   const int b = unit / sh.H, h = unit % sh.H;
+  const int tid = threadIdx.x;
+  const int attn_bytes = kMfma ? attn_region(D, RT) : 0;
+  const SelectPtrs p = select_ptrs(smem + attn_bytes, sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk,
+                                   sh.K);
+  // the unit's top-K list out, then the capped eviction (kk = list length)
+  auto finish = [&](int kk) {
+    __syncthreads();
+    for (int t = tid; t < sh.K; t += kThreads) {
+      if (t >= kk) p.sel_idx[t] = -1;
+      topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
+      topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
+    }
+    __syncthreads();
+    evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
+               p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
+               admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+  };
+  if constexpr (IL && kMfma) {
+    // Launched only when every context fits one scan part (one workgroup per
+    // unit): one pass streams the unit's blocks and its summary records
+    // together, two summary groups per block step (with 32 rows the query
+    // operands sit in LDS so that both groups fit 2 waves per SIMD).  The
+    // context length is read inside, after the query and slot-map loads.
+    const int nb = attn_scan_unit_bf16<D, RT, 2, 8, RT, (RT == 2)>(
+        sh, q, pool, p2l, summ + (size_t)unit * sh.NBmax * 2 * D, ctx + b, b, h, scale, out,
+        reinterpret_cast<float*>(smem), p.keys);
+    __syncthreads();
+    finish(topk_unit<kScanChunk / kThreads>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                            p.cand_key, p.ev.red));
+    return;
+  }
   const int L = ctx[b];
   const int nb = n_blocks(L, sh.NBmax);
   const int active = nb > kScanChunk ? 1 + scan_parts(nb) : 1;
@@ -398,10 +429,6 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   const bool whole = active == 1;          // one workgroup does the whole unit
   const int c0 = whole ? 0 : (part - 1) * kScanChunk;
   const int len = whole ? nb : (nb - c0 < kScanChunk ? nb - c0 : kScanChunk);
-  const int tid = threadIdx.x;
-  const int attn_bytes = kMfma ? attn_region(D, RT) : 0;
-  const SelectPtrs p = select_ptrs(smem + attn_bytes, sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk,
-                                   sh.K);
 
   auto attention = [&]() {
     if constexpr (kMfma)
@@ -419,18 +446,6 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   if (!whole) {
     if (part == 0) attention();
     else kk = scan_select();
-  } else if (IL && kMfma) {
-    // one pass streams the unit's blocks and its summary records together,
-    // two summary groups per block step (with 32 rows the query operands sit
-    // in LDS so that both groups fit 2 waves per SIMD)
-    if constexpr (IL && kMfma) {
-      attn_scan_unit_bf16<D, RT, 2, 8, RT, (RT == 2)>(
-          sh, q, pool, p2l, summ + (size_t)unit * sh.NBmax * 2 * D, nb, b, h, L, scale, out,
-          reinterpret_cast<float*>(smem), p.keys);
-      __syncthreads();
-      kk = topk_unit<kScanChunk / kThreads>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                            p.cand_key, p.ev.red);
-    }
   } else if (scan_first(unit)) {
     kk = scan_select();
     attention();
@@ -449,16 +464,7 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     if (tid == 0) ws.n[slot] = kk;
     return;                                // split_select_kernel finishes the unit
   }
-  __syncthreads();
-  for (int t = tid; t < sh.K; t += kThreads) {
-    if (t >= kk) p.sel_idx[t] = -1;
-    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
-    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
-  }
-  __syncthreads();
-  evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
-             p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
-             admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+  finish(kk);
 }
 
 // Second kernel of a split step: for every unit whose context exceeds

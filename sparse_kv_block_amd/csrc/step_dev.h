@@ -17,16 +17,18 @@
 namespace oasis {
 
 // Requires at most 64 slots per wave (K <= 256 with one row tile, K <= 128
-// with two).  Writes keys[j] for j < nb and the attention output; ends with the attention merge (so the keys are complete in LDS for
-// the whole workgroup afterwards).
+// with two).  Reads the request's context length from ctx_b (after issuing
+// the query and slot-map loads, so that the round trips overlap), writes
+// keys[j] for j < nb, returns nb, and ends with the attention merge (so the
+// keys are complete in LDS for the whole workgroup afterwards).
 template <int D, int RT, int SG, int UL, int TW = RT, bool QL = false>
-__device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ pool,
-                                                    const int32_t* __restrict__ p2l,
-                                                    const uint16_t* __restrict__ summ_unit, int nb,
-                                                    int b, int h, int L, float scale_log2,
-                                                    uint16_t* __restrict__ out, float* lds,
-                                                    uint32_t* keys) {
+__device__ __forceinline__ int attn_scan_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ pool,
+                                                   const int32_t* __restrict__ p2l,
+                                                   const uint16_t* __restrict__ summ_unit,
+                                                   const int32_t* __restrict__ ctx_b, int b, int h,
+                                                   float scale_log2, uint16_t* __restrict__ out,
+                                                   float* lds, uint32_t* keys) {
   using AW = AttnWave<D, RT, TW, QL>;
   constexpr int CPL = D / 16;
   constexpr int RW = CPL / 2;          // 32-bit words of one summary row slice
@@ -43,6 +45,8 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
   const int c0 = n * CPL;
   float Nq[CPL], Pq[CPL];
   group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Nq, Pq);
+  const int L = *ctx_b;
+  const int nb = n_blocks(L, sh.NBmax);
   if constexpr (QL) __syncthreads();
   // record groups: group t of wave w holds records 4*kWaves*t + 4*w + quad
   constexpr int GS = 4 * kWaves;
@@ -122,6 +126,7 @@ __device__ __forceinline__ void attn_scan_unit_bf16(const Shape& sh, const uint1
     score_groups(t, UL, lo, hi);
   }
   a.merge_store(sh, b, h, out, lds);
+  return nb;
 }
 
 }  // namespace oasis
