@@ -386,6 +386,51 @@ def test_fused_step_exact_on_integer_inputs(case):
     np.testing.assert_array_equal(i32(layer.admit_count), ref["count"])
 
 
+def random_case(seed: int):
+    """A seeded random shape: dtype, head dim, heads per KV head (1..16), KV
+    heads, K (1..256), slot-pool fill, cap, and per-request contexts within a
+    maximum block count that sometimes exceeds one scan part (the split path
+    then runs, also for the requests that fit one part)."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = "f32" if rng.random() < 0.2 else "bf16"
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.integers(1, 5))
+    G = int(rng.integers(1, 17))
+    batch = int(rng.integers(1, 9 // hkv + 1))
+    nbmax = int(rng.choice([64, 500, 1024, 1500] + ([] if dtype == "f32" else [4096])))
+    K = int(min(rng.choice([1, 3, 8, 16, 37, 64, 128, 256]), 256))
+    ctx = [int(rng.integers(0, nbmax * 16 + 1)) for _ in range(batch)]
+    ctx[int(rng.integers(batch))] = int(rng.integers(max(1, nbmax * 16 - 40), nbmax * 16 + 1))
+    cap = float(rng.choice([0.0, 0.05, 0.25, 0.5, 1.0, 1.0]))
+    fill = float(rng.choice([0.0, 0.5, 0.9, 1.0]))
+    cfg = small(dtype=dtype, head_dim=d, n_q_heads=G * hkv, n_kv_heads=hkv, batch=batch,
+                k_resident=K, cap=cap, planted=0)
+    return cfg, ctx, nbmax, fill
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fused_step_random_shapes_exact_on_integer_inputs(seed):
+    cfg, ctx, nbmax, fill = random_case(seed)
+    say(f"random case {seed}: {cfg.dtype} d={cfg.head_dim} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} "
+        f"K={cfg.k_resident} NBmax={nbmax} ctx={ctx} cap={cfg.cap} fill={fill}")
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=40 + seed, integer=True, nbmax=nbmax)
+    state = gen.random_state(cfg, ctx, nbmax, 40 + seed, fill=fill, stamp_max=3)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    layer.set_state(*state)
+    layer.pool.copy_(pool_from_records(rec, layer.p2l))
+    m = cfg.max_admit()
+    layer.step(q, 5, m)
+    ref = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, state, 5, m)
+    check_attention(layer.out, ref["out"], cfg.dtype, f"random case {seed}")
+    np.testing.assert_array_equal(i32(layer.topk_idx), ref["idx"])
+    for k in ("l2p", "p2l"):
+        np.testing.assert_array_equal(i32(getattr(layer, k)), ref[k])
+    np.testing.assert_array_equal(i32(layer.last_sel), ref["ls"])
+    np.testing.assert_array_equal(i32(layer.admit), ref["admit"])
+    np.testing.assert_array_equal(i32(layer.admit_count), ref["count"])
+
+
 # --------------------------------------------------------------------------- multi-step
 def run_steps(cfg, ctx, nbmax, rec, qseq, nsteps, units=None, what=""):
     """Carries the resident sets over decode steps on the GPU (fused step +
