@@ -510,9 +510,20 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(
   }
   __syncthreads();
   // at most 8192 / kScanChunk lists of K <= 256 entries
+  // keys per thread sized to the unit's list total (the selection's passes
+  // run over every register slot, filled or not; the result does not depend
+  // on the slot count)
   constexpr int kMergeKpt = (8192 / kScanChunk) * 256 / kThreads;
-  const int kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                      p.cand_key, p.ev.red);
+  int kk;
+  if (total <= kThreads)
+    kk = topk_unit<1>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  else if (total <= 2 * kThreads)
+    kk = topk_unit<2>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  else if (total <= 4 * kThreads)
+    kk = topk_unit<4>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  else
+    kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key,
+                              p.ev.red);
   for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
   __syncthreads();
   for (int t = tid; t < sh.K; t += kThreads) {
