@@ -129,11 +129,13 @@ __device__ __forceinline__ SelectPtrs select_ptrs(char* smem, int NBmax, int K) 
 
 // Top-K of the scores in p.keys[0..nb); leaves the sorted list in p.sel_idx
 // (entries past kk set to -1) and writes the top-K outputs of the unit.
+// KPT: keys per thread, at least nb / kThreads.
+template <int KPT = kMaxKpt>
 __device__ __forceinline__ void select_from_keys(const Shape& sh, int unit, int nb,
                                                  int32_t* topk_idx, float* topk_score,
                                                  const SelectPtrs& p) {
-  const int kk = topk_unit<kMaxKpt>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                     p.cand_key, p.ev.red);
+  const int kk = topk_unit<KPT>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
+                                p.cand_key, p.ev.red);
   for (int t = threadIdx.x; t < sh.K; t += kThreads) {
     if (t >= kk) p.sel_idx[t] = -1;
     topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
@@ -144,7 +146,7 @@ __device__ __forceinline__ void select_from_keys(const Shape& sh, int unit, int 
 
 // Scan + select for one unit; leaves the sorted list in p.sel_idx (entries
 // past kk set to -1) and writes the top-K outputs.
-template <typename T, int D, int U>
+template <typename T, int D, int U, int KPT>
 __device__ __forceinline__ void select_unit(const Shape& sh, const T* q, int q_row, const T* summ,
                                             int unit, int L, int32_t* topk_idx, float* topk_score,
                                             const SelectPtrs& p) {
@@ -152,10 +154,12 @@ __device__ __forceinline__ void select_unit(const Shape& sh, const T* q, int q_r
   const int nb = n_blocks(L, sh.NBmax);
   scan_unit<T, D, U>(sh, q, q_row, summ + (size_t)unit * sh.NBmax * 2 * D, b, h, nb, p.keys);
   __syncthreads();
-  select_from_keys(sh, unit, nb, topk_idx, topk_score, p);
+  select_from_keys<KPT>(sh, unit, nb, topk_idx, topk_score, p);
 }
 
-template <typename T, int D>
+// KPT = keys per thread of the top-K, chosen per launch from NBmax (the
+// selection's passes run over every register slot, filled or not).
+template <typename T, int D, int KPT>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T* __restrict__ q,
                                                               int q_row, const T* __restrict__ summ,
                                                               const int32_t* __restrict__ ctx,
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T*
   extern __shared__ __align__(16) char smem[];
   const int unit = blockIdx.x;
   const SelectPtrs p = select_ptrs(smem, sh.NBmax, sh.K);
-  select_unit<T, D, 4>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
+  select_unit<T, D, 4, KPT>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
 }
 
 // ------------------------------------------------------------------ agreement diagnostic
@@ -691,11 +695,16 @@ hipError_t launch_score_topk(const Shape& sh, int dtype, const void* q, int q_ro
                              hipStream_t st) {
   dim3 grid(sh.B * sh.H);
   const size_t lds = SelectLds(sh.NBmax, sh.K).total;
+  const bool small = sh.NBmax <= 4 * kThreads;     // 4 keys per thread suffice
 #define OASIS_SCORE(T_, D_)                                                                   \
-  hipLaunchKernelGGL((score_topk_kernel<T_, D_>), grid, dim3(kThreads), lds, st, sh,          \
-                     (const T_*)q, q_row, (const T_*)summ, ctx, topk_idx, topk_score)
-  if (dtype == 1) { if (sh.d == 128) OASIS_SCORE(uint16_t, 128); else OASIS_SCORE(uint16_t, 64); }
-  else            { if (sh.d == 128) OASIS_SCORE(float, 128);    else OASIS_SCORE(float, 64); }
+  if (small)                                                                                  \
+    hipLaunchKernelGGL((score_topk_kernel<T_, D_, 4>), grid, dim3(kThreads), lds, st, sh,     \
+                       (const T_*)q, q_row, (const T_*)summ, ctx, topk_idx, topk_score);      \
+  else                                                                                        \
+    hipLaunchKernelGGL((score_topk_kernel<T_, D_, kMaxKpt>), grid, dim3(kThreads), lds, st,   \
+                       sh, (const T_*)q, q_row, (const T_*)summ, ctx, topk_idx, topk_score)
+  if (dtype == 1) { if (sh.d == 128) { OASIS_SCORE(uint16_t, 128); } else { OASIS_SCORE(uint16_t, 64); } }
+  else            { if (sh.d == 128) { OASIS_SCORE(float, 128); }    else { OASIS_SCORE(float, 64); } }
 #undef OASIS_SCORE
   return hipGetLastError();
 }
