@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T*
 // top-K as the summary scan's.
 constexpr int kExactInFlight = 4;   // blocks per wave in flight (bf16)
 
-template <typename T, int D>
+template <typename T, int D, int KPT>
 __global__ __launch_bounds__(kThreads) void exact_topk_kernel(Shape sh, const T* __restrict__ q,
                                                               int q_row, const T* __restrict__ rec,
                                                               const int32_t* __restrict__ ctx,
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void exact_topk_kernel(Shape sh, const T*
   else
     exact_scan_f32<D>(sh, q, q_row, rec_unit, b, h, L, nb, p.keys);
   __syncthreads();
-  select_from_keys(sh, unit, nb, topk_idx, topk_score, p);
+  select_from_keys<KPT>(sh, unit, nb, topk_idx, topk_score, p);
 }
 
 // Per unit: entries among the first exact_n of the exact list that lie in
@@ -714,11 +714,16 @@ hipError_t launch_exact_topk(const Shape& sh, int dtype, const void* q, int q_ro
                              float* topk_score, hipStream_t st) {
   dim3 grid(sh.B * sh.H);
   const size_t lds = SelectLds(sh.NBmax, sh.K).total;
+  const bool small = sh.NBmax <= 4 * kThreads;     // 4 keys per thread suffice
 #define OASIS_EXACT(T_, D_)                                                                   \
-  hipLaunchKernelGGL((exact_topk_kernel<T_, D_>), grid, dim3(kThreads), lds, st, sh,          \
-                     (const T_*)q, q_row, (const T_*)records, ctx, topk_idx, topk_score)
-  if (dtype == 1) { if (sh.d == 128) OASIS_EXACT(uint16_t, 128); else OASIS_EXACT(uint16_t, 64); }
-  else            { if (sh.d == 128) OASIS_EXACT(float, 128);    else OASIS_EXACT(float, 64); }
+  if (small)                                                                                  \
+    hipLaunchKernelGGL((exact_topk_kernel<T_, D_, 4>), grid, dim3(kThreads), lds, st, sh,     \
+                       (const T_*)q, q_row, (const T_*)records, ctx, topk_idx, topk_score);   \
+  else                                                                                        \
+    hipLaunchKernelGGL((exact_topk_kernel<T_, D_, kMaxKpt>), grid, dim3(kThreads), lds, st,   \
+                       sh, (const T_*)q, q_row, (const T_*)records, ctx, topk_idx, topk_score)
+  if (dtype == 1) { if (sh.d == 128) { OASIS_EXACT(uint16_t, 128); } else { OASIS_EXACT(uint16_t, 64); } }
+  else            { if (sh.d == 128) { OASIS_EXACT(float, 128); }    else { OASIS_EXACT(float, 64); } }
 #undef OASIS_EXACT
   return hipGetLastError();
 }
