@@ -97,10 +97,33 @@ def cpu_baseline(cfg, ctx, records_host, qs_host, min_cpu_seconds: float):
                           l2p, p2l, ls, nthreads=nth)
         spent += time.perf_counter() - t0
         reps += 1
+    # one thread on a slice of the units (the same work per unit), scaled to a
+    # whole layer step
+    n1 = min(B * H, 64)
+    units = np.arange(n1, dtype=np.int32)
+    l2p, p2l, ls = [x.copy() for x in state]
+    t0 = time.perf_counter()
+    oracle.layer_step(q, rec, summ, ctx, cfg.block_size, cfg.k_resident, 1, cfg.max_admit(),
+                      l2p, p2l, ls, units=units, nthreads=1)
+    t1 = (time.perf_counter() - t0) * (B * H) / n1
     return {"value": reps / spent, "unit": "layer-steps/s", "cores": min(nth, B * H),
             "kind": "oracle",
             "sample": f"{reps} whole layer steps ({B * H} units each: attention, scan, top-K, "
-                      f"eviction) in {spent:.2f} s wall on {nth} threads"}
+                      f"eviction) in {spent:.2f} s wall on {nth} threads",
+            "single_thread": {"value": round(1.0 / t1, 4), "unit": "layer-steps/s",
+                              "sample": f"{n1} of {B * H} units on one thread, scaled"},
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def dense_leg(cfg, layer, rec, q, reps: int = 10):

@@ -63,3 +63,4 @@ def test_bench_prints_one_json_line_with_roofline_and_oracle_baseline():
     assert d["achievable"]["copy_GBps"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["single_thread"]["value"] > 0 and cb["cpu_model"]
