@@ -11,7 +11,8 @@ the host pool over the host link), the oracle reads the logical blocks, so
 attention parity also checks the prefetch.  Top-K lists must agree within the
 tolerance at the K-th score; maps, stamps and admissions bit for bit on every
 unit whose list agrees (a unit whose list differs inside the tolerance is set
-back to the oracle's state before the next step)."""
+back to the oracle's state before the next step).  Every unit of every layer
+is checked for the map invariants after each step."""
 import sys
 
 import numpy as np
@@ -104,6 +105,8 @@ def test_full_size_36_layer_pipeline_cap_sweep():
             dec.step(rec_host, [qs[l][t] for l in range(L)], t, m)
             dec.drain()
             torch.cuda.synchronize()
+            for l in range(L):
+                check_map_invariants(dec.layers[l], m, t, f"cap {cap} step {t} layer {l}")
             for l in check_layers:
                 layer = dec.layers[l]
                 for (b, h) in units:
@@ -134,6 +137,33 @@ def test_full_size_36_layer_pipeline_cap_sweep():
                         set_unit(layer, sl, o, u_dev[u])
             torch.cuda.synchronize()
     say(f"resyncs {resyncs}")
+
+
+def check_map_invariants(layer, m, t, what):
+    """Every unit of a layer: the slot map and the block map are inverse to each
+    other with no block held twice, at most m admissions, every admission's
+    slot holds its block and is stamped with the step, and every resident
+    member of the top-K list is stamped with the step."""
+    p2l = i32(layer.p2l)                                       # [B][H][K]
+    l2p = i32(layer.l2p)                                       # [B][H][NB]
+    ls = i32(layer.last_sel)
+    B, H, K = p2l.shape
+    bb, hh, ss = np.nonzero(p2l >= 0)
+    jj = p2l[bb, hh, ss]
+    assert np.array_equal(l2p[bb, hh, jj], ss), what
+    assert int((l2p >= 0).sum()) == len(jj), what             # no block mapped twice
+    cnt = i32(layer.admit_count)
+    assert cnt.min() >= 0 and cnt.max() <= m, what
+    adm = i32(layer.admit)                                     # [B][H][K][3]
+    for b, h in zip(*np.nonzero(cnt)):
+        a = adm[b, h, :cnt[b, h]]
+        assert np.array_equal(p2l[b, h, a[:, 1]], a[:, 0]), what
+        assert np.all(ls[b, h, a[:, 1]] == t), what
+    top = i32(layer.topk_idx)                                  # [B][H][K]
+    tb, th, tk = np.nonzero(top >= 0)
+    slot = l2p[tb, th, top[tb, th, tk]]
+    res = slot >= 0
+    assert np.all(ls[tb[res], th[res], slot[res]] == t), what
 
 
 def set_unit(layer, sl, o, rec_unit):
