@@ -31,28 +31,33 @@ def build(force: bool = True) -> str:
     return LIB_PATH
 
 
+def load(path: str):
+    """Opens a build of oracle.c and declares its functions' signatures."""
+    L = ctypes.CDLL(path)
+    P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    L.ora_summarize.argtypes = [I, I, I, I, I, I, P, P, P, P, I, I]
+    L.ora_block_scores.argtypes = [I, I, I, I, I, I, I, P, I, P, P, P, P, I, I]
+    L.ora_topk.argtypes = [I, I, I, I, I, P, P, P, P, P, I]
+    L.ora_max_admit.argtypes = [D, I]
+    L.ora_max_admit.restype = I
+    L.ora_capped_evict.argtypes = [I, I, I, I, P, ctypes.c_int32, ctypes.c_int32,
+                                   P, P, P, P, P, P, I]
+    L.ora_attention.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, D, P, P, I, I]
+    L.ora_prefetch.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, I]
+    L.ora_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
+    L.ora_exact_block_scores.argtypes = [I, I, I, I, I, I, I, P, I, P, P, P, P, I, I]
+    for f in (L.ora_summarize, L.ora_block_scores, L.ora_topk, L.ora_capped_evict,
+              L.ora_attention, L.ora_prefetch, L.ora_append, L.ora_exact_block_scores):
+        f.restype = None
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             build()
-        L = ctypes.CDLL(LIB_PATH)
-        P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
-        L.ora_summarize.argtypes = [I, I, I, I, I, I, P, P, P, P, I, I]
-        L.ora_block_scores.argtypes = [I, I, I, I, I, I, I, P, I, P, P, P, P, I, I]
-        L.ora_topk.argtypes = [I, I, I, I, I, P, P, P, P, P, I]
-        L.ora_max_admit.argtypes = [D, I]
-        L.ora_max_admit.restype = I
-        L.ora_capped_evict.argtypes = [I, I, I, I, P, ctypes.c_int32, ctypes.c_int32,
-                                       P, P, P, P, P, P, I]
-        L.ora_attention.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, D, P, P, I, I]
-        L.ora_prefetch.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, I]
-        L.ora_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
-        L.ora_exact_block_scores.argtypes = [I, I, I, I, I, I, I, P, I, P, P, P, P, I, I]
-        for f in (L.ora_summarize, L.ora_block_scores, L.ora_topk, L.ora_capped_evict,
-                  L.ora_attention, L.ora_prefetch, L.ora_append, L.ora_exact_block_scores):
-            f.restype = None
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 

@@ -210,8 +210,9 @@ def test_topk_matches_brute_force_ranks_with_ties(ora, seed):
 
 # --------------------------------------------------------------------------
 # Capped eviction
-def test_evict_worked_example(ora):
-    g = json.load(open(os.path.join(GOLDEN, "evict_worked_example.json")))
+@pytest.mark.parametrize("name", ["evict_worked_example.json", "evict_lrs_order_example.json"])
+def test_evict_worked_example(ora, name):
+    g = json.load(open(os.path.join(GOLDEN, name)))
     K, NB = g["K"], g["n_blocks"]
     p2l = np.array([[g["p2l_before"]]], np.int32)
     last = np.array([[g["last_sel_before"]]], np.int32)
@@ -260,6 +261,24 @@ def check_evict_invariants(T, step, m, before, after, admit, count):
                 if p2l1[b, h, s] in set(t):
                     assert ls1[b, h, s] == step
             assert np.all(admit[b, h, a:] == -1)
+            # victim order: empty slots first, in slot order; then the least
+            # recently selected resident blocks outside the top-K, by (stamp,
+            # block).  Stamps are the ones before this step (a top-K member is
+            # never a candidate, so its refresh to `step` does not matter).
+            slots = admit[b, h, :a, 1].tolist()
+            empties = [s for s in range(K) if p2l0[b, h, s] < 0]
+            assert slots[:filled] == empties[:filled], "empty slots are filled first, in slot order"
+            if filled < a:
+                assert filled == empty0, "a resident block is evicted only once no slot is empty"
+            cand = [(int(ls0[b, h, s]), int(p2l0[b, h, s]), s) for s in range(K)
+                    if p2l0[b, h, s] >= 0 and p2l0[b, h, s] not in set(t) and ls0[b, h, s] < step]
+            chosen = [(int(ls0[b, h, s]), int(p2l0[b, h, s]), s) for s in slots[filled:]]
+            assert chosen == sorted(chosen), "victims are taken least recently selected first"
+            kept = [c for c in cand if c[2] not in set(slots)]
+            if chosen and kept:
+                assert max(chosen) < min(kept), (
+                    "every evicted block was selected no more recently than every kept stale block "
+                    "(ties: lower block first)")
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -277,6 +296,67 @@ def test_evict_invariants_random(ora, seed):
     before = (l2p.copy(), p2l.copy(), ls.copy())
     admit, count = ora.capped_evict(T, 5, m, l2p, p2l, ls)
     check_evict_invariants(T, 5, m, before, (l2p, p2l, ls), admit, count)
+
+
+def random_evict_case(rng):
+    """A consistent random state of a few units: K slots, NB blocks, a fill,
+    stamps below the step (some at or above it: never victims), a top-K list
+    of distinct blocks (fewer than K when the request is short) and a cap."""
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    K = int(rng.integers(1, 17))
+    NB = int(rng.integers(1, 40))
+    step = int(rng.integers(1, 9))
+    l2p = np.full((B, H, NB), -1, np.int32)
+    p2l = np.full((B, H, K), -1, np.int32)
+    ls = rng.integers(0, step + 2, size=(B, H, K)).astype(np.int32)
+    T = np.full((B, H, K), -1, np.int32)
+    for b in range(B):
+        for h in range(H):
+            n = int(rng.integers(0, min(K, NB) + 1))
+            blocks = rng.choice(NB, size=n, replace=False)
+            slots = rng.choice(K, size=n, replace=False)
+            p2l[b, h, slots] = blocks
+            l2p[b, h, blocks] = slots
+            nt = int(rng.integers(0, min(K, NB) + 1))
+            T[b, h, :nt] = rng.choice(NB, size=nt, replace=False)
+    m = int(rng.integers(0, K + 2))
+    return T, step, m, l2p, p2l, ls
+
+
+def assert_evict_matches_numpy(ora, T, step, m, l2p, p2l, ls):
+    import evict_np
+    want = evict_np.capped_evict(T, step, m, l2p, p2l, ls)
+    before = (l2p.copy(), p2l.copy(), ls.copy())
+    admit, count = ora.capped_evict(T, step, m, l2p, p2l, ls)
+    for name, got, exp in zip(("l2p", "p2l", "last_sel", "admit", "admit_count"),
+                              (l2p, p2l, ls, admit, count), want):
+        np.testing.assert_array_equal(got, exp, err_msg=f"{name} differs from the numpy eviction")
+    return before, admit, count
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_evict_matches_independent_numpy_eviction(ora, seed):
+    rng = np.random.default_rng(700 + seed)
+    T, step, m, l2p, p2l, ls = random_evict_case(rng)
+    before, admit, count = assert_evict_matches_numpy(ora, T, step, m, l2p, p2l, ls)
+    if np.all(before[2] < step):
+        check_evict_invariants(T, step, m, before, (l2p, p2l, ls), admit, count)
+
+
+def test_evict_matches_numpy_at_full_unit_size(ora):
+    # one batch of the Qwen3-8B shape's per-unit sizes: K = 128 slots over 1024
+    # blocks, cap 0.05 (6 admissions), stamps spread over the previous steps
+    cfg = QWEN3_8B_16K.scaled(batch=4)
+    ctx = gen.context_lengths(cfg)
+    nbmax = cfg.max_blocks()
+    l2p, p2l, ls = [x.numpy().copy() for x in gen.random_state(cfg, ctx, nbmax, 3, fill=0.97,
+                                                               stamp_max=9)]
+    scores = np.random.default_rng(3).normal(size=(cfg.batch, cfg.n_kv_heads, nbmax))
+    T, _ = ora.topk(scores, ctx, cfg.block_size, cfg.k_resident)
+    m = ora.max_admit(cfg.cap, cfg.k_resident)
+    before, admit, count = assert_evict_matches_numpy(ora, T, 9, m, l2p, p2l, ls)
+    check_evict_invariants(T, 9, m, before, (l2p, p2l, ls), admit, count)
+    assert int(count.min()) == m
 
 
 def test_evict_zero_cap_only_stamps(ora):
