@@ -44,11 +44,12 @@ def log(*a):
 
 def algorithmic_bytes(cfg, ctx: np.ndarray) -> dict:
     """Bytes the fused step must move per launch (one layer, whole batch)."""
+    from sparse_kv_block_amd import lib
     B, H, K, d, Hq = cfg.batch, cfg.n_kv_heads, cfg.k_resident, cfg.head_dim, cfg.n_q_heads
     es = cfg.esize
     S = cfg.block_size
     nb = np.minimum(-(-ctx.astype(np.int64) // S), cfg.max_blocks(int(ctx.max())))
-    m = cfg.max_admit()
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
     kv = B * H * K * 2 * S * d * es                       # resident records (keys + values)
     summ = int(H * nb.sum()) * 2 * d * es                  # min/max rows of every block
     q_out = 2 * (B * 2 * Hq * d * es)                      # queries read, outputs written
@@ -93,7 +94,8 @@ def cpu_baseline(cfg, ctx, records_host, qs_host, min_cpu_seconds: float):
     while spent * nth < min_cpu_seconds or reps == 0:
         l2p, p2l, ls = [x.copy() for x in state]
         t0 = time.perf_counter()
-        oracle.layer_step(q, rec, summ, ctx, cfg.block_size, cfg.k_resident, 1, cfg.max_admit(),
+        oracle.layer_step(q, rec, summ, ctx, cfg.block_size, cfg.k_resident, 1,
+                          oracle.max_admit(cfg.cap, cfg.k_resident),
                           l2p, p2l, ls, nthreads=nth)
         spent += time.perf_counter() - t0
         reps += 1
@@ -103,7 +105,8 @@ def cpu_baseline(cfg, ctx, records_host, qs_host, min_cpu_seconds: float):
     units = np.arange(n1, dtype=np.int32)
     l2p, p2l, ls = [x.copy() for x in state]
     t0 = time.perf_counter()
-    oracle.layer_step(q, rec, summ, ctx, cfg.block_size, cfg.k_resident, 1, cfg.max_admit(),
+    oracle.layer_step(q, rec, summ, ctx, cfg.block_size, cfg.k_resident, 1,
+                      oracle.max_admit(cfg.cap, cfg.k_resident),
                       l2p, p2l, ls, units=units, nthreads=1)
     t1 = (time.perf_counter() - t0) * (B * H) / n1
     return {"value": reps / spent, "unit": "layer-steps/s", "cores": min(nth, B * H),
@@ -222,7 +225,7 @@ def kernels_leg(cfg, layer, ctx, nbmax, qs, rec, reps: int = 10):
     byt = sum_blocks * 2 * cfg.head_dim * es + q.numel() * es // 2 + units * cfg.k_resident * 8
     out["score_topk"] = {"us": round(us, 1), "bytes": byt, "GBps": round(byt / us / 1e3, 1)}
     saved = layer.state()
-    m = cfg.max_admit()
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
 
     def restore():
         layer.set_state(*saved)
@@ -390,7 +393,7 @@ def capmodel_leg(cfg, layer, rec_host, ctx, nbmax, qs, t_layer_s: float, gather:
         measured = {row["cap"]: row["step_ms"] for row in pipeline["caps"]}
         moved = {row["cap"]: row["bytes_per_step"] for row in pipeline["caps"]}
     for cap in caps:
-        m = cfg.max_admit(cap)
+        m = lib.cap_to_max_admit(cap, cfg.k_resident)
         nbytes = cm.bytes_per_step(layers, units, m, rec_bytes)
         out["predicted_step_ms"].append({
             "cap": cap, "max_admit": m, "bytes": nbytes,
@@ -433,7 +436,7 @@ def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
            "host_pool": "one pinned pool shared by all layers", "caps": []}
     main = torch.cuda.current_stream()
     for cap in cfg.caps_sweep:
-        m = cfg.max_admit(cap)
+        m = lib.cap_to_max_admit(cap, cfg.k_resident)
         dec.setup(rec_host, [qs[l][1] for l in range(L)], summ_from=src_layer)
         torch.cuda.synchronize()
         admitted = torch.zeros((), dtype=torch.int64, device=dev)
@@ -536,7 +539,7 @@ def main():
     nbmax = cfg.max_blocks(int(ctx.max()))
     nq = args.query_sets
     log(f"[bench] {cfg.name}: B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} d={cfg.head_dim} "
-        f"NBmax={nbmax} K={cfg.k_resident} m={cfg.max_admit()}")
+        f"NBmax={nbmax} K={cfg.k_resident} m={lib.cap_to_max_admit(cfg.cap, cfg.k_resident)}")
     qseq = gen.query_sequence(cfg, nq + 1, device=dev)
     dirs = gen.planted_directions(cfg, qseq[1]) if cfg.planted else None
     qs = [gen.step_queries(cfg, qseq, s) for s in range(1, nq + 1)]

@@ -24,7 +24,7 @@ class Config:
     block_size: int            # S tokens per block
     ctx: Optional[int]         # fixed context length per request, or None (lognormal)
     k_resident: int            # K resident blocks per (request, KV head)
-    cap: float                 # per-step fetch ratio cap
+    cap: float                 # per-step fetch ratio cap (admissions: oasis_cap_to_max_admit)
     draft_sigma: float         # draft = next-step query + N(0, draft_sigma)
     rho: float                 # AR(1) coefficient of the query drift between steps
     planted: int = 0           # high-affinity blocks per (request, KV head)
@@ -57,14 +57,6 @@ class Config:
         lmax = ctx_max if ctx_max is not None else (
             self.ctx if self.ctx is not None else self.ctx_lognormal[3])
         return -(-lmax // self.block_size)
-
-    def max_admit(self, cap: Optional[float] = None) -> int:
-        """Admissions allowed per (request, KV head) per step: floor(cap*K), with a
-        1e-9 guard so that products such as 0.05*128 = 6.4 or 0.25*8 = 2 are not
-        lost to binary rounding."""
-        c = self.cap if cap is None else cap
-        import math
-        return int(math.floor(c * self.k_resident + 1e-9))
 
     def scaled(self, **kw) -> "Config":
         return replace(self, **kw)

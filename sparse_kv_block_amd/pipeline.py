@@ -38,6 +38,8 @@ class Layer:
         self.admit = torch.full((B, H, K, 3), -1, dtype=torch.int32, device=device)
         self.admit_count = torch.zeros((B, H), dtype=torch.int32, device=device)
         self.workspace = lib.layer_step_workspace(self.shape, device)
+        # admissions per unit and step at the workload's cap (the library's rule)
+        self.max_admit = lib.cap_to_max_admit(cfg.cap, K)
 
     # ------------------------------------------------------------------ setup
     def summarize(self, records):
@@ -58,7 +60,10 @@ class Layer:
     def append(self, records, k_new: torch.Tensor, v_new: torch.Tensor):
         """Decode append of one token per request ([B][Hkv][d] keys and values):
         into `records`, the resident copy of its block when resident, and the
-        block's summary; this layer's context lengths grow by one."""
+        block's summary; this layer's context lengths grow by one.  Enqueued on
+        the current stream: the caller orders it after any prefetch still
+        filling this layer's slots (`Decoder.append` does), or a gather that
+        read the record before the append could overwrite the slot after it."""
         lib.append_token(self.shape, k_new, v_new, records, self.summ, self.ctx_len,
                          pool=self.pool, l2p=self.l2p)
 
@@ -73,7 +78,7 @@ class Layer:
     # ------------------------------------------------------------------ per step
     def step(self, q: torch.Tensor, step: int, max_admit: Optional[int] = None, scale: float = 0.0):
         """Fused look-ahead layer step (attention, scan, top-K, eviction)."""
-        m = self.cfg.max_admit() if max_admit is None else max_admit
+        m = self.max_admit if max_admit is None else max_admit
         lib.layer_step(self.shape, q, self.pool, self.summ, self.ctx_len, step, m, self.out,
                        self.topk_idx, self.topk_score, self.l2p, self.p2l, self.last_sel,
                        self.admit, self.admit_count, scale=scale, workspace=self.workspace)
@@ -81,7 +86,7 @@ class Layer:
     def step_unfused(self, q: torch.Tensor, step: int, max_admit: Optional[int] = None,
                      scale: float = 0.0):
         """The same step as four separate C-ABI calls."""
-        m = self.cfg.max_admit() if max_admit is None else max_admit
+        m = self.max_admit if max_admit is None else max_admit
         lib.lookahead_attn(self.shape, q, self.pool, self.p2l, self.ctx_len, self.out, scale=scale)
         lib.score_topk(self.shape, q, self.summ, self.ctx_len, self.topk_idx, self.topk_score, q_row=1)
         lib.capped_evict(self.shape, self.topk_idx, step, m, self.l2p, self.p2l, self.last_sel,
@@ -89,7 +94,7 @@ class Layer:
 
     def prefetch(self, records, max_admit: Optional[int] = None, mode: int = lib.GATHER,
                  host_staging=None, side_stream=None, wait_before=None, done=None):
-        m = self.cfg.max_admit() if max_admit is None else max_admit
+        m = self.max_admit if max_admit is None else max_admit
         lib.prefetch(self.shape, records, self.pool, self.admit, self.admit_count, m, mode=mode,
                      host_staging=host_staging, side_stream=side_stream,
                      wait_before=wait_before, done=done)
@@ -139,7 +144,7 @@ class Decoder:
         """One decode step over all layers; qs[i] is layer i's query tensor.
         `before_prefetch(i)` (optional) is enqueued on the side stream before
         layer i's prefetch (tests use it to delay the side stream)."""
-        m = self.cfg.max_admit() if max_admit is None else max_admit
+        m = self.layers[0].max_admit if max_admit is None else max_admit
         main = torch.cuda.current_stream()
         if mode == lib.MEMCPY and self.staging is None:
             n = self.layers[0].shape.units() * (3 * self.cfg.k_resident + 1)
@@ -156,6 +161,13 @@ class Decoder:
             layer.prefetch(records, m, mode=mode, host_staging=self.staging,
                            side_stream=self.side, wait_before=self.ev_sel[i], done=self.ev_pf[i])
             self.pending[i] = True
+
+    def append(self, i: int, records, k_new: torch.Tensor, v_new: torch.Tensor):
+        """Decode append into layer i (see `Layer.append`), ordered after that
+        layer's pending prefetch on the side stream."""
+        if self.pending[i]:
+            torch.cuda.current_stream().wait_event(self.ev_pf[i])
+        self.layers[i].append(records, k_new, v_new)
 
     def drain(self):
         main = torch.cuda.current_stream()

@@ -30,7 +30,7 @@ def check_attention(out_gpu: torch.Tensor, out_ora: np.ndarray, dtype: str, what
 
 
 def check_topk(idx_gpu: np.ndarray, sc_gpu: np.ndarray, idx_ora: np.ndarray, scores_ora: np.ndarray,
-               what="", exact=False):
+               what="", exact=False, differ_units=None):
     """Top-K parity per unit.  The lists must have the same length; every block
     in their symmetric difference must score within TOPK_REL (relative) of the
     oracle's K-th score; position r of the GPU list must hold a block whose
@@ -53,6 +53,8 @@ def check_topk(idx_gpu: np.ndarray, sc_gpu: np.ndarray, idx_ora: np.ndarray, sco
                 continue
             assert not exact, f"{what} unit ({b},{h}): top-K lists differ on exact inputs"
             differ += 1
+            if differ_units is not None:
+                differ_units.append((b, h))
             s_row = scores_ora[b, h]
             kth = s_row[io[n - 1]]
             tol = TOPK_REL * abs(kth)
@@ -95,3 +97,108 @@ def pool_from_records(records: torch.Tensor, p2l: torch.Tensor) -> torch.Tensor:
     pool = torch.gather(records, 2, idx[..., None].expand(-1, -1, -1, records.shape[-1]))
     pool[p2l < 0] = 0
     return pool.contiguous()
+
+
+def tie_exposed(scores_ora: np.ndarray, K: int) -> np.ndarray:
+    """Per unit: whether two of the oracle's K+1 best scores lie within TOPK_REL
+    (relative to its K-th score) of each other.  Only such a unit can have a
+    GPU top-K list that differs from the oracle's inside the tolerance (a swap
+    needs two scores closer than the fp32 rounding of the GPU's sums, which is
+    far below TOPK_REL), so the count of differing units is bounded by the
+    count of exposed ones."""
+    B, H, NB = scores_ora.shape
+    n = min(K + 1, NB)
+    top = -np.sort(-scores_ora.reshape(B * H, NB), axis=1)[:, :n]
+    out = np.zeros(B * H, bool)
+    for u in range(B * H):
+        s = top[u][np.isfinite(top[u])]
+        if s.size < 2:
+            continue
+        kth = s[min(K, s.size) - 1]
+        out[u] = bool(np.any(s[:-1] - s[1:] <= TOPK_REL * abs(kth)))
+    return out.reshape(B, H)
+
+
+def summaries_equal_by_value(got: np.ndarray, ref: np.ndarray) -> bool:
+    """Summaries compared by value: bit-identical, except that +0 and -0 are
+    equal (a min or max of equal values may keep either sign of zero)."""
+    if got.dtype == np.uint16:
+        same = got == ref
+        zero = ((got & 0x7FFF) == 0) & ((ref & 0x7FFF) == 0)
+        return bool(np.all(same | zero))
+    return bool(np.all(got == ref))
+
+
+class OracleTwin:
+    """The oracle's copy of one layer's resident state, stepped beside a GPU
+    `Layer` on the same inputs and compared with it in full after every call.
+
+    Attention is compared within the tolerance; the top-K list per unit within
+    the tolerance at the K-th score (R21 of the readings: a list that differs
+    must differ only among scores within TOPK_REL of each other); then the
+    oracle evicts with the GPU's (validated) list, so that every unit's block
+    maps, stamps and admissions are compared bit for bit at every step, also
+    where the lists differed, and the two states never part."""
+
+    def __init__(self, cfg, rec_cpu, ctx, summ=None):
+        self.cfg = cfg
+        self.rec = rec_cpu
+        self.ctx = np.ascontiguousarray(np.asarray(ctx, np.int32))
+        self.summ = oracle.summarize(rec_cpu, self.ctx, 16) if summ is None else summ
+        B, H, NB = rec_cpu.shape[0], rec_cpu.shape[1], rec_cpu.shape[2]
+        K = cfg.k_resident
+        self.l2p = np.full((B, H, NB), -1, np.int32)
+        self.p2l = np.full((B, H, K), -1, np.int32)
+        self.ls = np.zeros((B, H, K), np.int32)
+        self.unit_steps = 0
+        self.differ = []
+        self.exposed = 0
+
+    def check_summaries(self, layer, what=""):
+        assert summaries_equal_by_value(host(layer.summ), self.summ), f"{what}: summaries differ"
+
+    def _topk(self, layer, q_cpu, q_row, what):
+        K = self.cfg.k_resident
+        sc = oracle.block_scores(q_cpu, self.summ, self.ctx, 16, q_row=q_row)
+        idx, _ = oracle.topk(sc, self.ctx, 16, K)
+        differ_units = []
+        check_topk(i32(layer.topk_idx), host(layer.topk_score), idx, sc, what=what,
+                   differ_units=differ_units)
+        exposed = tie_exposed(sc, K)
+        for (b, h) in differ_units:
+            assert exposed[b, h], f"{what} unit ({b},{h}): lists differ without a near-tie"
+        self.unit_steps += exposed.size
+        self.exposed += int(exposed.sum())
+        self.differ += [(what, b, h) for (b, h) in differ_units]
+        return i32(layer.topk_idx)
+
+    def _maps(self, layer, admit, count, what):
+        np.testing.assert_array_equal(i32(layer.l2p), self.l2p, err_msg=f"{what}: l2p")
+        np.testing.assert_array_equal(i32(layer.p2l), self.p2l, err_msg=f"{what}: p2l")
+        np.testing.assert_array_equal(i32(layer.last_sel), self.ls, err_msg=f"{what}: last_sel")
+        np.testing.assert_array_equal(i32(layer.admit), admit, err_msg=f"{what}: admit")
+        np.testing.assert_array_equal(i32(layer.admit_count), count, err_msg=f"{what}: admit_count")
+
+    def cold_fill(self, layer, q_cpu, what=""):
+        """After layer.cold_fill(q): the normal row's top-K into empty slots at step 0."""
+        T = self._topk(layer, q_cpu, 0, f"{what} cold fill")
+        self.l2p.fill(-1)
+        self.p2l.fill(-1)
+        self.ls.fill(0)
+        K = self.cfg.k_resident
+        admit, count = oracle.capped_evict(T, 0, K, self.l2p, self.p2l, self.ls)
+        self._maps(layer, admit, count, f"{what} cold fill")
+
+    def step(self, layer, q_cpu, step, m, what=""):
+        """After layer.step(q, step, m): attention over the state before the
+        step, then the draft row's top-K and the capped eviction."""
+        out = oracle.attention(q_cpu, self.rec, self.p2l, self.ctx, 16)
+        check_attention(layer.out, out, self.cfg.dtype, f"{what} step {step}")
+        T = self._topk(layer, q_cpu, 1, f"{what} step {step}")
+        admit, count = oracle.capped_evict(T, step, m, self.l2p, self.p2l, self.ls)
+        self._maps(layer, admit, count, f"{what} step {step}")
+        return admit, count
+
+    def report(self):
+        return (f"{self.unit_steps} unit-steps compared in full, {len(self.differ)} top-K lists "
+                f"differed inside the tolerance (bound: {self.exposed} unit-steps with a near-tie)")

@@ -167,7 +167,7 @@ def test_agreement_study_matches_oracle_composition():
     say("agreement study vs oracle")
     rec, _ = gen.integer_inputs(cfg, ctx, nbmax, seed=11, device=DEV)
     qs = gen.integer_queries(cfg, 10, seed=12, device=DEV)
-    m = cfg.max_admit()
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
     layer = Layer(cfg, ctx, nbmax)
     layer.summarize(rec)
     layer.cold_fill(qs[0], rec)

@@ -1,16 +1,14 @@
 """GPU parity: every C-ABI call against the CPU oracle on seeded inputs.
 
-Small shapes are compared element by element; the full-size workloads are
-compared on sampled units (each sampled (request, KV head) pair is cut out as a
-one-request, one-KV-head problem for the oracle, which is exact because every
-step of the method is local to its unit).
+Small shapes, element by element.  The five workloads at their full sizes,
+carried over decode steps and compared unit by unit in full, are in
+test_gpu_full_size.py and test_gpu_full36.py.
 
 Tolerances: maps, admissions and summaries bit-exact (summaries by value);
 top-K exact except swaps within 1e-5 relative of the K-th score (and exact on
 small-integer inputs, where every score is exact in fp32); attention within
 1e-2 (bf16) or 1e-5 (fp32) absolute + relative of the fp64 oracle.
 """
-import math
 import sys
 
 import numpy as np
@@ -18,10 +16,9 @@ import pytest
 import torch
 
 import oracle
-from parity import (ATTN_TOL, check_attention, check_topk, host, i32, pool_from_records,
-                    sample_units, unit_slice)
+from parity import check_attention, check_topk, host, i32, pool_from_records
 from sparse_kv_block_amd import gen
-from sparse_kv_block_amd.configs import AGENTIC, GQA16, QWEN3_8B_16K, TINY, Config
+from sparse_kv_block_amd.configs import Config
 
 pytestmark = pytest.mark.gpu
 
@@ -374,7 +371,7 @@ def test_fused_step_exact_on_integer_inputs(case):
     layer.summarize(rec)
     layer.set_state(*state)
     layer.pool.copy_(pool_from_records(rec, layer.p2l))
-    m = cfg.max_admit()
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
     layer.step(q, 5, m)
     ref = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, state, 5, m)
     check_attention(layer.out, ref["out"], cfg.dtype)
@@ -419,7 +416,7 @@ def test_fused_step_random_shapes_exact_on_integer_inputs(seed):
     layer.summarize(rec)
     layer.set_state(*state)
     layer.pool.copy_(pool_from_records(rec, layer.p2l))
-    m = cfg.max_admit()
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
     layer.step(q, 5, m)
     ref = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, state, 5, m)
     check_attention(layer.out, ref["out"], cfg.dtype, f"random case {seed}")
@@ -429,149 +426,6 @@ def test_fused_step_random_shapes_exact_on_integer_inputs(seed):
     np.testing.assert_array_equal(i32(layer.last_sel), ref["ls"])
     np.testing.assert_array_equal(i32(layer.admit), ref["admit"])
     np.testing.assert_array_equal(i32(layer.admit_count), ref["count"])
-
-
-# --------------------------------------------------------------------------- multi-step
-def run_steps(cfg, ctx, nbmax, rec, qseq, nsteps, units=None, what=""):
-    """Carries the resident sets over decode steps on the GPU (fused step +
-    gather prefetch) and on the oracle.  Maps must agree bit for bit on every
-    unit whose top-K list agrees; a unit whose list differs inside the
-    tolerance is set back to the oracle's state before the next step.
-    `units`: compare only these (b, h) pairs, each as its own oracle problem."""
-    G, m = cfg.group, cfg.max_admit()
-    layer = Layer(cfg, ctx, nbmax)
-    layer.summarize(rec)
-    q1 = gen.step_queries(cfg, qseq, 1)
-    layer.cold_fill(q1, rec)
-    rec_cpu = {}
-    if units is None:
-        units = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_kv_heads)]
-        whole = True
-    else:
-        whole = False
-    # oracle cold fill on its own summaries: the normal query's top-K into empty slots
-    ora = {}
-    for key in ([None] if whole else units):
-        b, h = key if key is not None else (0, 0)
-        if whole:
-            r = rec.cpu()
-            c = ctx
-        else:
-            r = unit_slice(rec, b, h, G, "unit").cpu()
-            c = unit_slice(ctx, b, h, G, "ctx")
-        qq = q1.cpu() if whole else unit_slice(q1, b, h, G, "q").cpu()
-        summ = oracle.summarize(r, c, 16)
-        sc = oracle.block_scores(qq, summ, c, 16, q_row=0)
-        idx, _ = oracle.topk(sc, c, 16, cfg.k_resident)
-        nb = r.shape[2]
-        Bn, Hn = r.shape[0], r.shape[1]
-        l2p = np.full((Bn, Hn, nb), -1, np.int32)
-        p2l = np.full((Bn, Hn, cfg.k_resident), -1, np.int32)
-        ls = np.zeros((Bn, Hn, cfg.k_resident), np.int32)
-        oracle.capped_evict(idx, 0, cfg.k_resident, l2p, p2l, ls)
-        ora[key] = dict(rec=r, ctx=c, summ=summ, l2p=l2p, p2l=p2l, ls=ls)
-    resyncs = 0
-
-    def resync(key, o):
-        nonlocal resyncs
-        resyncs += 1
-        sl = (slice(None),) * 3 if whole else (slice(key[0], key[0] + 1), slice(key[1], key[1] + 1))
-        layer.l2p[sl] = torch.from_numpy(o["l2p"]).to(DEV)
-        layer.p2l[sl] = torch.from_numpy(o["p2l"]).to(DEV)
-        layer.last_sel[sl] = torch.from_numpy(o["ls"]).to(DEV)
-        layer.pool[sl] = pool_from_records(rec[sl] if not whole else rec, layer.p2l[sl])
-
-    # the cold fill itself
-    torch.cuda.synchronize()
-    for key, o in ora.items():
-        sl = (slice(None),) * 3 if whole else (slice(key[0], key[0] + 1), slice(key[1], key[1] + 1))
-        if not (np.array_equal(i32(layer.p2l[sl]), o["p2l"]) and
-                np.array_equal(i32(layer.l2p[sl]), o["l2p"])):
-            resync(key, o)
-    for step in range(1, nsteps + 1):
-        q = gen.step_queries(cfg, qseq, step)
-        say(f"{what} step {step}")
-        layer.step(q, step, m)
-        layer.prefetch(rec, m)
-        torch.cuda.synchronize()
-        for key, o in ora.items():
-            b, h = key if key is not None else (None, None)
-            sl = (slice(None),) * 3 if whole else (slice(b, b + 1), slice(h, h + 1))
-            qq = q.cpu() if whole else unit_slice(q, b, h, G, "q").cpu()
-            out, idx, val, admit, count = oracle.layer_step(
-                qq, o["rec"], o["summ"], o["ctx"], 16, cfg.k_resident, step, m,
-                o["l2p"], o["p2l"], o["ls"])
-            sc = oracle.block_scores(qq, o["summ"], o["ctx"], 16)
-            gout = layer.out if whole else layer.out[b:b + 1, :, h * G:(h + 1) * G]
-            check_attention(gout, out, cfg.dtype, f"{what} step {step} unit {key}")
-            gidx = i32(layer.topk_idx[sl])
-            differ = check_topk(gidx, host(layer.topk_score[sl]), idx, sc,
-                                what=f"{what} step {step}")
-            if differ == 0:
-                np.testing.assert_array_equal(i32(layer.l2p[sl]), o["l2p"])
-                np.testing.assert_array_equal(i32(layer.p2l[sl]), o["p2l"])
-                np.testing.assert_array_equal(i32(layer.last_sel[sl]), o["ls"])
-                np.testing.assert_array_equal(i32(layer.admit[sl]), admit)
-                np.testing.assert_array_equal(i32(layer.admit_count[sl[:2]]), count)
-            else:
-                resync(key, o)
-    return resyncs
-
-
-def test_tiny_f32_config_multi_step():
-    cfg = TINY.scaled(steps=4)
-    ctx = gen.context_lengths(cfg)
-    nbmax = cfg.max_blocks()
-    qseq = gen.query_sequence(cfg, 6, device=DEV)
-    rec = gen.records(cfg, ctx, nbmax, device=DEV)
-    run_steps(cfg, ctx, nbmax, rec, qseq, 4, what="tiny")
-
-
-def test_agentic_shape_reduced_batch_32_steps():
-    # the long-context agentic shape (lognormal contexts, 8K-128K) on 3 requests,
-    # all units, 32 carried steps with AR(1) drift
-    cfg = AGENTIC.scaled(batch=3)
-    ctx = gen.context_lengths(cfg)
-    nbmax = cfg.max_blocks(int(ctx.max()))
-    say("agentic contexts", ctx.tolist())
-    qseq = gen.query_sequence(cfg, cfg.steps + 1, device=DEV)
-    rec = gen.records(cfg, ctx, nbmax, device=DEV)
-    resyncs = run_steps(cfg, ctx, nbmax, rec, qseq, cfg.steps, what="agentic-b3")
-    say("resyncs", resyncs)
-
-
-# --------------------------------------------------------------------------- full sizes
-def full_size_check(cfg: Config, n_units: int, steps: int):
-    ctx = gen.context_lengths(cfg)
-    nbmax = cfg.max_blocks(int(ctx.max()))
-    say(f"{cfg.name}: generating B={cfg.batch} NBmax={nbmax}")
-    qseq = gen.query_sequence(cfg, steps + 1, device=DEV)
-    dirs = gen.planted_directions(cfg, qseq[1]) if cfg.planted else None
-    rec = gen.records(cfg, ctx, nbmax, device=DEV, planted_dir=dirs)
-    units = sample_units(cfg.batch, cfg.n_kv_heads, n_units, cfg.seed)
-    say(f"{cfg.name}: units {units}")
-    resyncs = run_steps(cfg, ctx, nbmax, rec, qseq, steps, units=units, what=cfg.name)
-    say(f"{cfg.name}: resyncs {resyncs}")
-    # summaries of the sampled units
-    layer_summ = Layer(cfg, ctx, nbmax)
-    layer_summ.summarize(rec)
-    for (b, h) in units[:4]:
-        r = unit_slice(rec, b, h, cfg.group, "unit").cpu()
-        ref = oracle.summarize(r, unit_slice(ctx, b, h, cfg.group, "ctx"), 16)
-        np.testing.assert_array_equal(oracle.to_f64(host(layer_summ.summ[b:b + 1, h:h + 1])),
-                                      oracle.to_f64(ref))
-
-
-def test_full_size_qwen3_8b_16k():
-    full_size_check(QWEN3_8B_16K, 12, 2)
-
-
-def test_full_size_gqa16():
-    full_size_check(GQA16, 8, 2)
-
-
-def test_full_size_agentic():
-    full_size_check(AGENTIC, 8, 3)
 
 
 # --------------------------------------------------------------------------- edge cases
@@ -596,7 +450,7 @@ def test_fused_step_edge_cases(case):
     layer.summarize(rec)
     layer.set_state(*state)
     layer.pool.copy_(pool_from_records(rec, layer.p2l))
-    m = max(1, cfg.max_admit())
+    m = max(1, lib.cap_to_max_admit(cfg.cap, cfg.k_resident))
     layer.step(q, 3, m)
     ref = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, state, 3, m)
     check_attention(layer.out, ref["out"], cfg.dtype, str(case))

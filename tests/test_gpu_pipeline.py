@@ -62,7 +62,7 @@ def test_decoder_layers_match_oracle(records_on, delay):
     qs = [gen.integer_queries(cfg, n_steps + 1, seed=100 + i, device="cuda") for i in range(n_layers)]
     dec = Decoder(cfg, ctx, nb, n_layers)
     dec.setup(records, [qs[i][0] for i in range(n_layers)])
-    m = cfg.max_admit()
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
     # a long spin on the side stream before every prefetch: if the next step's
     # attention did not wait for the layer's prefetch it would read stale slots
     slow = (lambda i: torch.cuda._sleep(20_000_000)) if delay else None
@@ -89,6 +89,50 @@ def test_decoder_layers_match_oracle(records_on, delay):
             assert int(count.sum()) > 0, "the inputs should force admissions"
 
 
+@pytest.mark.parametrize("records_on", ["pinned", "device"])
+def test_decoder_append_between_pipelined_steps(records_on):
+    # a token per request is appended to the layer after every step, while the
+    # step's prefetch (delayed on the side stream) may still be filling slots
+    cfg = cfg_small(batch=3)
+    n_steps = 5
+    ctx = np.array([1000, 31, 700], np.int32)        # the second crosses into a new block
+    nb = cfg.max_blocks() + 1
+    rec_cpu, _ = gen.integer_inputs(cfg, ctx, nb, seed=5)
+    records = rec_cpu.pin_memory() if records_on == "pinned" else rec_cpu.cuda()
+    qs = gen.integer_queries(cfg, n_steps + 1, seed=77, device="cuda")
+    kn, vn = gen.new_tokens(cfg, n_steps, seed=78, device="cuda", integer=True)
+    dec = Decoder(cfg, ctx, nb, 1)
+    dec.setup(records, [qs[0]])
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
+    slow = lambda i: torch.cuda._sleep(20_000_000)      # noqa: E731
+    got = []
+    for t in range(1, n_steps + 1):
+        dec.step(records, [qs[t]], t, m, before_prefetch=slow)
+        L = dec.layers[0]
+        got.append((L.out.clone(), L.topk_idx.clone(), L.p2l.clone(), L.admit.clone()))
+        dec.append(0, records, kn[t - 1], vn[t - 1])
+    dec.drain()
+    torch.cuda.synchronize()
+    ora = OracleLayer(cfg, rec_cpu.clone(), ctx.copy(), qs[0].cpu())
+    rec_np = oracle.as_np(ora.rec)
+    for t in range(1, n_steps + 1):
+        out, idx, _, admit, count = ora.step(qs[t].cpu(), t, m)
+        what = f"step {t}"
+        check_attention(got[t - 1][0], out, "bf16", what)
+        np.testing.assert_array_equal(i32(got[t - 1][1]), idx, err_msg=what)
+        np.testing.assert_array_equal(i32(got[t - 1][2]), ora.p2l, err_msg=what)
+        np.testing.assert_array_equal(i32(got[t - 1][3]), admit, err_msg=what)
+        oracle.append(kn[t - 1].cpu(), vn[t - 1].cpu(), rec_np, ora.summ, ora.ctx, 16)
+    L = dec.layers[0]
+    np.testing.assert_array_equal(i32(L.ctx_len), ora.ctx)
+    assert np.array_equal(host(records), rec_np)
+    np.testing.assert_array_equal(oracle.to_f64(host(L.summ)), oracle.to_f64(ora.summ))
+    p2l = i32(L.p2l).astype(np.int64)
+    pool = host(L.pool)
+    b, h, s = np.nonzero(p2l >= 0)
+    assert np.array_equal(pool[b, h, s], rec_np[b, h, p2l[b, h, s]]), "resident copies"
+
+
 def test_memcpy_mode_pipeline():
     cfg = cfg_small()
     ctx = np.array([1000, 333], np.int32)
@@ -99,7 +143,7 @@ def test_memcpy_mode_pipeline():
     dec = Decoder(cfg, ctx, nb, 2)
     dec.setup(records, [qs[0], qs[0]])
     ora = [OracleLayer(cfg, rec_cpu, ctx, qs[0].cpu()) for _ in range(2)]
-    m = cfg.max_admit()
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
     for t in range(1, 4):
         dec.step(records, [qs[t], qs[t]], t, m, mode=lib.MEMCPY)
         outs = [L.out.clone() for L in dec.layers]

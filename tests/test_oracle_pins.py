@@ -463,8 +463,8 @@ def test_prefetch_copies_whole_records(ora):
 # Cap rounding and the byte model against the pages' numbers
 def test_cap_rounding(ora):
     assert [ora.max_admit(c, 128) for c in (0.0, 0.01, 0.05, 0.2, 1.0)] == [0, 1, 6, 25, 128]
-    assert ora.max_admit(0.25, 8) == 2 == TINY.max_admit()
-    assert QWEN3_8B_16K.max_admit() == 6
+    assert ora.max_admit(0.25, 8) == 2 == ora.max_admit(TINY.cap, TINY.k_resident)
+    assert ora.max_admit(QWEN3_8B_16K.cap, QWEN3_8B_16K.k_resident) == 6
 
 
 def test_bytes_per_step_at_cap_001_is_the_pages_030_gb(ora):
