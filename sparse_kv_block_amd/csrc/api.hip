@@ -1,12 +1,13 @@
 // C-ABI of liboasis: argument validation, error reporting and dispatch to the
-// gfx950 launchers.  Declarations and contracts: include/oasis.h.
+// gfx950 launchers.  Declarations and contracts: include/oasis.h.  Host code
+// only (HIP runtime API and the launchers of launch.h), so that it also builds
+// as plain C++ for the sanitizer test of its validation and copy planning.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
 #include <string>
 
-#include "common.h"
 #include "launch.h"
 #include "oasis.h"
 
@@ -312,8 +313,7 @@ size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape) {
   if (!shape || shape->n_kv_heads <= 0 || shape->batch <= 0 || shape->max_blocks <= 0 ||
       shape->k_resident <= 0)
     return 0;
-  return oasis::step_workspace_bytes(shape->batch * shape->n_kv_heads,
-                                     oasis::step_parts(shape->max_blocks), shape->k_resident);
+  return oasis::layer_step_workspace_bytes(to_shape(shape));
 }
 
 oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const void* pool,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace oasis {
 
 constexpr int kWave = 64;
@@ -19,10 +21,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-struct Shape {
-  int B, Hq, H, G, d, NBmax, K;
-};
 
 __device__ __forceinline__ int n_blocks(int L, int NBmax) {
   if (L <= 0) return 0;

@@ -832,6 +832,10 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
   return hipGetLastError();
 }
 
+size_t layer_step_workspace_bytes(const Shape& sh) {
+  return step_workspace_bytes(sh.B * sh.H, step_parts(sh.NBmax), sh.K);
+}
+
 size_t dense_workspace_bytes(const Shape& sh) {
   const int chunks = (sh.NBmax + kDenseChunk - 1) / kDenseChunk;
   return (size_t)sh.B * sh.H * chunks * 2 * sh.G * (sh.d + 2) * sizeof(float);

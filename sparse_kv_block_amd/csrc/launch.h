@@ -1,13 +1,23 @@
 // Internal launchers: the kernels' translation unit exports these to the
-// C-ABI layer.  Arguments are already validated by the caller.
+// C-ABI layer.  Arguments are already validated by the caller.  Host code
+// only: the C-ABI layer includes nothing else from the kernels.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace oasis {
 
-struct Shape;
+// Validated problem shape: B requests, Hq query heads, H KV heads, G = Hq / H,
+// head dim d, NBmax blocks per unit in the record and summary arrays, K slots.
+struct Shape {
+  int B, Hq, H, G, d, NBmax, K;
+};
+
+// Bytes of the fused step's split-scan workspace for a shape (0 when every
+// context fits one scan part).
+size_t layer_step_workspace_bytes(const Shape& sh);
 
 hipError_t launch_summarize(const Shape& sh, int dtype, const void* records,
                             const int32_t* ctx_len, void* summ, hipStream_t st);
