@@ -107,8 +107,9 @@ def test_full_size_36_layer_pipeline_cap_sweep():
             exposed += twins[l].exposed
             unit_steps += twins[l].unit_steps
         torch.cuda.synchronize()
-    say(f"{unit_steps} unit-steps compared in full, {differ} top-K lists differed inside the "
-        f"tolerance (bound: {exposed} unit-steps with a near-tie)")
+    say(f"{unit_steps} unit-steps compared in full, {differ} top-K lists differed, each only "
+        f"between blocks within the fp32 rounding scale of each other (bound: {exposed} "
+        f"unit-steps with such a near-tie)")
     assert differ <= exposed
 
 
