@@ -44,8 +44,10 @@
  *
  *  Ownership.  Every buffer belongs to the caller; device pointers are HIP
  *  device (or host-mapped) addresses on the current device.  The library keeps
- *  no state between calls except a thread-local error string.  No call
- *  allocates device memory.
+ *  no state between calls except a thread-local error string and the
+ *  per-device scratch of oasis_layer_step_noalloc (a device array in the
+ *  library's code object, not an allocation).  No call allocates device
+ *  memory.
  *
  *  Asynchrony.  Each call enqueues its work on the given HIP stream (a
  *  hipStream_t passed as void*, NULL = the null stream) and returns without
@@ -271,6 +273,27 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q,
                               int32_t* admit, int32_t* admit_count,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* The fused step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same launches and results as oasis_layer_step, with the split-scan
+ * lists kept in the library's own device scratch instead of a workspace
+ * argument.  The scratch is a 32 MiB array per device, held from the first
+ * call on that device until the process ends; shapes whose lists exceed it
+ * (oasis_layer_step_workspace_bytes above 32 MiB) return
+ * OASIS_ERR_UNSUPPORTED.  The call allocates nothing.  All calls on one device
+ * share its scratch: calls that may overlap on one device (other streams,
+ * other threads) race and must be ordered by the caller.  The first call on a
+ * device looks up the scratch's address (hipGetSymbolAddress); it is not
+ * captured into a graph, so make one call before a capture begins. */
+oasis_status oasis_layer_step_noalloc(const oasis_shape* shape, const void* q,
+                                      const void* pool, const void* summ,
+                                      const int32_t* ctx_len, float scale,
+                                      int32_t step, int32_t max_admit, void* out,
+                                      int32_t* topk_idx, float* topk_score,
+                                      int32_t* l2p, int32_t* p2l,
+                                      int32_t* last_sel, int32_t* admit,
+                                      int32_t* admit_count, void* stream);
 
 /* Dense comparator (not part of the look-ahead method) — decode attention of
  * both rows of every query head over every valid token of the full KV,

@@ -91,7 +91,7 @@ size_t esize(const oasis_shape* s) { return s->dtype == OASIS_DTYPE_F32 ? 4 : 2;
 
 extern "C" {
 
-int32_t oasis_abi_version(void) { return 6; }
+int32_t oasis_abi_version(void) { return 7; }
 
 const char* oasis_last_error(void) { return g_error.c_str(); }
 
@@ -316,16 +316,27 @@ size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape) {
   return oasis::layer_step_workspace_bytes(to_shape(shape));
 }
 
-oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const void* pool,
-                              const void* summ, const int32_t* ctx_len, float scale, int32_t step,
-                              int32_t max_admit, void* out, int32_t* topk_idx, float* topk_score,
-                              int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
-                              int32_t* admit_count, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  const char* fn = "oasis_layer_step";
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by oasis_layer_step (caller's workspace) and
+// oasis_layer_step_noalloc (the library's scratch, `use_scratch`).
+oasis_status layer_step_impl(const char* fn, bool use_scratch, const oasis_shape* shape,
+                             const void* q, const void* pool, const void* summ,
+                             const int32_t* ctx_len, float scale, int32_t step, int32_t max_admit,
+                             void* out, int32_t* topk_idx, float* topk_score, int32_t* l2p,
+                             int32_t* p2l, int32_t* last_sel, int32_t* admit, int32_t* admit_count,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   if (oasis_status st = check_shape(shape, fn)) return st;
   if (max_admit < 0) return fail(OASIS_ERR_INVALID, "%s: max_admit %d < 0", fn, max_admit);
   if (isnan(scale) || isinf(scale)) return fail(OASIS_ERR_INVALID, "%s: scale is not finite", fn);
+  const size_t need = oasis_layer_step_workspace_bytes(shape);
+  if (use_scratch && need > oasis::kScratchBytes)
+    return fail(OASIS_ERR_UNSUPPORTED,
+                "%s: this shape needs %zu bytes of split-scan lists, above the library's "
+                "%zu-byte scratch (oasis_layer_step takes a workspace of any size)",
+                fn, need, oasis::kScratchBytes);
   if (shape->batch == 0) return OASIS_OK;
   OASIS_NONNULL(q, fn);
   OASIS_NONNULL(pool, fn);
@@ -339,8 +350,9 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const voi
   OASIS_NONNULL(last_sel, fn);
   OASIS_NONNULL(admit, fn);
   OASIS_NONNULL(admit_count, fn);
-  const size_t need = oasis_layer_step_workspace_bytes(shape);
-  if (need > 0) {
+  if (need > 0 && use_scratch) {
+    if (oasis_status s = hip_status(oasis::scratch_pointer(&workspace), fn)) return s;
+  } else if (need > 0) {
     OASIS_NONNULL(workspace, fn);
     if (workspace_bytes < need)
       return fail(OASIS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
@@ -353,6 +365,32 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const voi
                                              p2l, last_sel, admit, admit_count,
                                              need > 0 ? workspace : nullptr, (hipStream_t)stream),
                     fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+oasis_status oasis_layer_step(const oasis_shape* shape, const void* q, const void* pool,
+                              const void* summ, const int32_t* ctx_len, float scale, int32_t step,
+                              int32_t max_admit, void* out, int32_t* topk_idx, float* topk_score,
+                              int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                              int32_t* admit_count, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return layer_step_impl("oasis_layer_step", false, shape, q, pool, summ, ctx_len, scale, step,
+                         max_admit, out, topk_idx, topk_score, l2p, p2l, last_sel, admit,
+                         admit_count, workspace, workspace_bytes, stream);
+}
+
+oasis_status oasis_layer_step_noalloc(const oasis_shape* shape, const void* q, const void* pool,
+                                      const void* summ, const int32_t* ctx_len, float scale,
+                                      int32_t step, int32_t max_admit, void* out,
+                                      int32_t* topk_idx, float* topk_score, int32_t* l2p,
+                                      int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                                      int32_t* admit_count, void* stream) {
+  return layer_step_impl("oasis_layer_step_noalloc", true, shape, q, pool, summ, ctx_len, scale,
+                         step, max_admit, out, topk_idx, topk_score, l2p, p2l, last_sel, admit,
+                         admit_count, nullptr, 0, stream);
 }
 
 size_t oasis_dense_attn_workspace_bytes(const oasis_shape* shape) {

@@ -6,6 +6,8 @@
 // synchronisation.  At batch 128 x 8 KV heads that is 1024 workgroups; the
 // fused step's register use (about 220 VGPRs, two waves per SIMD) places two
 // per CU, so they run in two even rounds over the 256 CUs.
+#include <mutex>
+
 #include "attn_dev.h"
 #include "diag_dev.h"
 #include "launch.h"
@@ -830,6 +832,38 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
                        admit_count, parts, ws);
   }
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ scratch
+// Device memory for the callers that cannot allocate (oasis_layer_step_noalloc):
+// the fused step's split-scan lists.  Each device that loads the library holds
+// its own copy until the process ends.  Host code never uses the array's name
+// as an address: the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_pointer(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 size_t layer_step_workspace_bytes(const Shape& sh) {

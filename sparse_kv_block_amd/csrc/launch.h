@@ -19,6 +19,11 @@ struct Shape {
 // context fits one scan part).
 size_t layer_step_workspace_bytes(const Shape& sh);
 
+// The library's own device scratch (oasis_layer_step_noalloc): its size, and
+// its address on the current device (looked up on the first call per device).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_pointer(void** ptr);
+
 hipError_t launch_summarize(const Shape& sh, int dtype, const void* records,
                             const int32_t* ctx_len, void* summ, hipStream_t st);
 hipError_t launch_attn(const Shape& sh, int dtype, const void* q, const void* pool,

@@ -29,7 +29,8 @@ SYMBOLS = ("oasis_abi_version", "oasis_last_error", "oasis_cap_to_max_admit",
            "oasis_summarize", "oasis_lookahead_attn", "oasis_score_topk",
            "oasis_capped_evict", "oasis_prefetch", "oasis_layer_step",
            "oasis_layer_step_workspace_bytes", "oasis_dense_attn", "oasis_dense_attn_workspace_bytes",
-           "oasis_append_token", "oasis_exact_topk", "oasis_topk_agreement")
+           "oasis_append_token", "oasis_exact_topk", "oasis_topk_agreement",
+           "oasis_layer_step_noalloc")
 
 
 class OasisError(RuntimeError):
@@ -82,6 +83,7 @@ def _load():
         "oasis_layer_step": ([SP, P, P, P, P, F, I32, I32, P, P, P, P, P, P, P, P, P,
                               ctypes.c_size_t, P], I32),
         "oasis_layer_step_workspace_bytes": ([SP], ctypes.c_size_t),
+        "oasis_layer_step_noalloc": ([SP, P, P, P, P, F, I32, I32, P, P, P, P, P, P, P, P, P], I32),
         "oasis_dense_attn": ([SP, P, P, P, F, P, P, ctypes.c_size_t, P], I32),
         "oasis_dense_attn_workspace_bytes": ([SP], ctypes.c_size_t),
         "oasis_append_token": ([SP, P, P, P, P, P, P, P, P], I32),
@@ -299,6 +301,23 @@ def layer_step(shape: Shape, q, pool, summ, ctx_len, step: int, max_admit: int, 
         _dev(l2p, "l2p", I32, U * shape.max_blocks), _dev(p2l, "p2l", I32, U * K),
         _dev(last_sel, "last_sel", I32, U * K), _dev(admit, "admit", I32, U * K * 3),
         _dev(admit_count, "admit_count", I32, U), *_workspace(shape, workspace), _stream(stream)))
+
+
+def layer_step_noalloc(shape: Shape, q, pool, summ, ctx_len, step: int, max_admit: int, out,
+                       topk_idx, topk_score, l2p, p2l, last_sel, admit, admit_count,
+                       scale: float = 0.0, stream=None):
+    """The fused step with the library's own device scratch (no workspace; see
+    oasis_layer_step_noalloc)."""
+    dt, U, K, d = shape.torch_dtype(), shape.units(), shape.k_resident, shape.head_dim
+    qn = shape.batch * 2 * shape.n_q_heads * d
+    _check(_lib.oasis_layer_step_noalloc(
+        ctypes.byref(shape), _dev(q, "q", dt, qn), _dev(pool, "pool", dt, U * K * shape.record_elems()),
+        _dev(summ, "summ", dt, U * shape.max_blocks * 2 * d), _dev(ctx_len, "ctx_len", I32, shape.batch),
+        float(scale), int(step), int(max_admit), _dev(out, "out", dt, qn),
+        _dev(topk_idx, "topk_idx", I32, U * K), _dev(topk_score, "topk_score", torch.float32, U * K),
+        _dev(l2p, "l2p", I32, U * shape.max_blocks), _dev(p2l, "p2l", I32, U * K),
+        _dev(last_sel, "last_sel", I32, U * K), _dev(admit, "admit", I32, U * K * 3),
+        _dev(admit_count, "admit_count", I32, U), _stream(stream)))
 
 
 def dense_attn_workspace(shape: Shape, device="cuda"):

@@ -40,12 +40,19 @@ const char* hipGetErrorString(hipError_t e) { return e == hipSuccess ? "no error
 // ---------------------------------------------------------- launcher stubs
 static int g_launches = 0;
 static int g_last_gather_admit = -1;
+static unsigned char g_scratch_stub[256] __attribute__((aligned(256)));
+static int g_scratch_lookups = 0;
 
 namespace oasis {
 size_t layer_step_workspace_bytes(const Shape& sh) {
   return sh.NBmax > 1024 ? (size_t)sh.B * sh.H * 4096 : 0;
 }
 size_t dense_workspace_bytes(const Shape& sh) { return (size_t)sh.B * sh.H * 64; }
+hipError_t scratch_pointer(void** ptr) {
+  ++g_scratch_lookups;
+  *ptr = g_scratch_stub;
+  return hipSuccess;
+}
 hipError_t launch_summarize(const Shape&, int, const void*, const int32_t*, void*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
@@ -222,6 +229,33 @@ static void check_layer_step_workspace() {
         OASIS_OK);
 }
 
+static void check_layer_step_noalloc() {
+  oasis_shape s = good_shape();
+  char d[64];
+  int32_t c[4] = {0, 0, 0, 0};
+  float* f = (float*)d;
+  const int before = g_launches, looked = g_scratch_lookups;
+  // fits one scan part: no scratch needed
+  CHECK(oasis_layer_step_noalloc(&s, d, d, d, c, 0.f, 1, 6, d, c, f, c, c, c, c, c, nullptr) ==
+        OASIS_OK);
+  CHECK(g_scratch_lookups == looked);
+  // split scan within the scratch
+  s.max_blocks = 3000;
+  CHECK(oasis_layer_step_noalloc(&s, d, d, d, c, 0.f, 1, 6, d, c, f, c, c, c, c, c, nullptr) ==
+        OASIS_OK);
+  CHECK(g_scratch_lookups == looked + 1);
+  CHECK(g_launches == before + 2);
+  CHECK(oasis_layer_step_noalloc(&s, d, d, d, c, 0.f, 1, 6, nullptr, c, f, c, c, c, c, c,
+                                 nullptr) == OASIS_ERR_INVALID);
+  CHECK(strstr(oasis_last_error(), "oasis_layer_step_noalloc") != nullptr);
+  // lists larger than the scratch are refused before anything is launched
+  s.batch = (int)(oasis::kScratchBytes / 4096 / s.n_kv_heads) + 1;
+  CHECK(oasis_layer_step_workspace_bytes(&s) > oasis::kScratchBytes);
+  CHECK(oasis_layer_step_noalloc(&s, d, d, d, c, 0.f, 1, 6, d, c, f, c, c, c, c, c, nullptr) ==
+        OASIS_ERR_UNSUPPORTED);
+  CHECK(g_launches == before + 2);
+}
+
 static void check_helpers() {
   CHECK(oasis_cap_to_max_admit(0.05, 128) == 6);
   CHECK(oasis_cap_to_max_admit(0.25, 8) == 2);
@@ -333,6 +367,7 @@ int main() {
   check_shape_validation();
   check_null_arguments();
   check_layer_step_workspace();
+  check_layer_step_noalloc();
   check_helpers();
   for (unsigned seed = 0; seed < 200; ++seed) check_memcpy_prefetch(seed);
   check_memcpy_runs_merge();

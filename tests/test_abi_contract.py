@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_helpers(L, ora):
     raw = L.raw()
-    assert raw.oasis_abi_version() == 6
+    assert raw.oasis_abi_version() == 7
     for cap, K in [(0.0, 128), (0.01, 128), (0.05, 128), (0.2, 128), (1.0, 128), (0.25, 8),
                    (2.0, 16), (-1.0, 8), (0.3, 10), (0.7, 10)]:
         assert L.cap_to_max_admit(cap, K) == ora.max_admit(cap, K), (cap, K)
