@@ -410,22 +410,22 @@ def capmodel_leg(cfg, layer, rec_host, ctx, nbmax, qs, t_layer_s: float, gather:
     return out
 
 
-def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
+def pipeline_leg(src_layer, rec_host, steps: int, warmup: int, gather_GBps=None):
     """The 36-layer decode step with the fetch-cap sweep: per layer the fused
     step on the main stream and the gather prefetch of its admissions on a side
     stream, layer-local events between them.  One host pool serves all layers
     (36 per-layer 8 GiB pools would exceed the host memory of one box); each
     layer has its own queries, resident pool and summaries in HBM."""
     import torch
-    from sparse_kv_block_amd import gen, lib
+    from sparse_kv_block_amd import capmodel as cm
+    from sparse_kv_block_amd import gen
     from sparse_kv_block_amd.configs import FULL_36
-    from sparse_kv_block_amd.pipeline import Decoder
+    from sparse_kv_block_amd.pipeline import Decoder, time_cap_sweep
     cfg = FULL_36
     ctx = gen.context_lengths(cfg)
     nbmax = cfg.max_blocks()
     L = cfg.layers
     dev = "cuda"
-    rec_bytes = 2 * cfg.block_size * cfg.head_dim * cfg.esize
     dec = Decoder(cfg, ctx, nbmax, L, device=dev)
     n_q = warmup + steps + 1
     qs = []
@@ -434,51 +434,18 @@ def pipeline_leg(src_layer, rec_host, steps: int, warmup: int):
         qs.append([None] + [gen.step_queries(cfg, seq, t, seed=1000 * 4 + l) for t in range(1, n_q + 1)])
     out = {"layers": L, "batch": cfg.batch, "ctx": int(ctx.max()), "k_resident": cfg.k_resident,
            "host_pool": "one pinned pool shared by all layers", "caps": []}
-    main = torch.cuda.current_stream()
-    for cap in cfg.caps_sweep:
-        m = lib.cap_to_max_admit(cap, cfg.k_resident)
-        dec.setup(rec_host, [qs[l][1] for l in range(L)], summ_from=src_layer)
-        torch.cuda.synchronize()
-        admitted = torch.zeros((), dtype=torch.int64, device=dev)
-        t = 0
-        for _ in range(warmup):
-            t += 1
-            dec.step(rec_host, [qs[l][t] for l in range(L)], t, m)
-        dec.drain()
-        torch.cuda.synchronize()
-        admitted.zero_()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        h0 = time.perf_counter()
-        a.record(main)
-        for _ in range(steps):
-            t += 1
-            dec.step(rec_host, [qs[l][t] for l in range(L)], t, m)
-            for layer in dec.layers:
-                admitted += layer.admit_count.sum()
-        dec.drain()
-        b.record(main)
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - h0) / steps
-        dev_s = a.elapsed_time(b) / 1e3 / steps
-        # the same steps without the host link: fused kernels only
-        c, d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c.record(main)
-        for _ in range(steps):
-            for l, layer in enumerate(dec.layers):
-                layer.step(qs[l][t], t + 1, 0)
-        d.record(main)
-        torch.cuda.synchronize()
-        comp_s = c.elapsed_time(d) / 1e3 / steps
-        moved = int(admitted.item()) * rec_bytes / steps
-        row = {"cap": cap, "max_admit": m, "bytes_per_step": moved,
-               "bytes_bound": cfg.batch * cfg.n_kv_heads * L * m * rec_bytes,
-               "step_ms": round(dev_s * 1e3, 3), "wall_ms": round(wall * 1e3, 3),
-               "compute_only_ms": round(comp_s * 1e3, 3),
-               "host_link_GBps": round(moved / dev_s / 1e9, 2),
-               "attention_path_tokens_per_s": round(cfg.batch / dev_s, 1)}
+    rows = time_cap_sweep(dec, rec_host, qs, cfg.caps_sweep, steps, warmup, summ_from=src_layer)
+    for row in rows:
+        row["attention_path_tokens_per_s"] = round(cfg.batch / (row["step_ms"] / 1e3), 1)
+        if gather_GBps:
+            xfer_s = row["bytes_per_step"] / (gather_GBps * 1e9)
+            row["transfer_alone_ms"] = round(xfer_s * 1e3, 3)
+            row["overlap_fraction"] = round(cm.overlap_fraction(
+                row["step_ms"] / 1e3, row["compute_only_ms"] / 1e3, xfer_s), 3)
         out["caps"].append(row)
-        log(f"[bench] 36 layers cap {cap} (m={m}): {moved / 1e9:.3f} GB/step, step {dev_s * 1e3:.2f} ms, "
-            f"fused kernels alone {comp_s * 1e3:.2f} ms")
+        log(f"[bench] 36 layers cap {row['cap']} (m={row['max_admit']}): "
+            f"{row['bytes_per_step'] / 1e9:.3f} GB/step, step {row['step_ms']:.2f} ms, "
+            f"fused kernels alone {row['compute_only_ms']:.2f} ms")
     del dec
     torch.cuda.empty_cache()
     return out
@@ -641,6 +608,11 @@ def main():
                      "avg_kernel_us": round(avg_kernel_s * 1e6, 2),
                      "median_kernel_us": round(median_kernel_us, 2)},
     }
+    # one layer step's latency (the tiny workload's figure of merit)
+    result["latency_us"] = {"avg": round(avg_kernel_s * 1e6, 2), "median": round(median_kernel_us, 2),
+                            "min": round(min(kern_ms) * 1e3, 2),
+                            "kind": "fused layer step on the GPU, HIP events (avg over the timed "
+                                    "steps; median and min of 20 single launches)"}
     result["achievable"] = achievable_leg(args.copy_probe_mib)
 
     if not args.no_pcie:
@@ -677,7 +649,10 @@ def main():
         dense["sparse_step_speedup"] = round(dense["us"] / (avg_kernel_s * 1e6), 2)
         result["dense_comparator"] = dense
     if args.pipeline:
-        result["pipeline_36_layer"] = pipeline_leg(layer, rec_host, args.pipeline_steps, 2)
+        result["pipeline_36_layer"] = pipeline_leg(
+            layer, rec_host, args.pipeline_steps, 2,
+            gather_GBps=(result["pcie"]["gather"]["bytes"] / result["pcie"]["gather"]["device_s"] / 1e9
+                         if "pcie" in result else None))
 
     if args.kernels:
         result["per_kernel"] = kernels_leg(cfg, layer, ctx, nbmax, qs, rec_dev)

@@ -40,3 +40,13 @@ def predicted_step_s(window_s: float, nbytes: float, bandwidth: float,
     larger of the two), or serialised after it."""
     xfer = nbytes / bandwidth if bandwidth > 0 else math.inf
     return max(window_s, xfer) if overlap else window_s + xfer
+
+
+def overlap_fraction(step_s: float, compute_s: float, xfer_s: float) -> float:
+    """Share of the shorter of the compute window and the transfer that the
+    pipelined step hid behind the other: (compute + transfer - step) /
+    min(compute, transfer), clipped to [0, 1] (1 = fully hidden, 0 = serial)."""
+    shorter = min(compute_s, xfer_s)
+    if shorter <= 0:
+        return 1.0
+    return max(0.0, min(1.0, (compute_s + xfer_s - step_s) / shorter))

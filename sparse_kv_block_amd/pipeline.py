@@ -8,7 +8,8 @@ and written by `append`.  Every method enqueues C-ABI calls on the current strea
 """
 from __future__ import annotations
 
-from typing import Optional
+import time
+from typing import Optional, Sequence
 
 import numpy as np
 import torch
@@ -174,3 +175,65 @@ class Decoder:
         for i in range(len(self.layers)):
             if self.pending[i]:
                 main.wait_event(self.ev_pf[i])
+
+
+def time_cap_sweep(dec: Decoder, records, qs, caps: Sequence[float], steps: int, warmup: int,
+                   summ_from: Optional[Layer] = None):
+    """The pipelined decode step of every layer of `dec` at each fetch cap.
+
+    Per cap: cold fill (`Decoder.setup`), `warmup` untimed steps, then `steps`
+    timed steps (the fused step of each layer on the current stream, its
+    gather prefetch on the side stream, layer-local events), bracketed by two
+    events on the current stream after a drain; then the same number of steps
+    with no admissions (the fused kernels alone).  qs[l][t] is layer l's query
+    tensor at step t (t >= 1; qs[l][0] unused).  Returns one row per cap:
+    admissions allowed per unit (max_admit, from the library's cap rule),
+    bytes moved per step (from the admission counts) and their bound
+    (layers * units * max_admit * record bytes), step and compute-only times,
+    and the host-link rate the step sustained."""
+    L = len(dec.layers)
+    shape = dec.layers[0].shape
+    K = shape.k_resident
+    units = shape.units()
+    rec_bytes = lib.record_bytes(shape)
+    main = torch.cuda.current_stream()
+    rows = []
+    for cap in caps:
+        m = lib.cap_to_max_admit(cap, K)
+        dec.setup(records, [qs[l][1] for l in range(L)], summ_from=summ_from)
+        torch.cuda.synchronize()
+        t = 0
+        for _ in range(warmup):
+            t += 1
+            dec.step(records, [qs[l][t] for l in range(L)], t, m)
+        dec.drain()
+        torch.cuda.synchronize()
+        admitted = torch.zeros((), dtype=torch.int64, device=dec.layers[0].device)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        a.record(main)
+        for _ in range(steps):
+            t += 1
+            dec.step(records, [qs[l][t] for l in range(L)], t, m)
+            for layer in dec.layers:
+                admitted += layer.admit_count.sum()
+        dec.drain()
+        b.record(main)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - h0) / steps
+        step_s = a.elapsed_time(b) / 1e3 / steps
+        c, d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c.record(main)
+        for _ in range(steps):
+            for l, layer in enumerate(dec.layers):
+                layer.step(qs[l][t], t + 1, 0)
+        d.record(main)
+        torch.cuda.synchronize()
+        compute_s = c.elapsed_time(d) / 1e3 / steps
+        moved = int(admitted.item()) * rec_bytes / steps
+        rows.append({"cap": cap, "max_admit": m, "bytes_per_step": moved,
+                     "bytes_bound": units * L * m * rec_bytes,
+                     "step_ms": round(step_s * 1e3, 3), "wall_ms": round(wall * 1e3, 3),
+                     "compute_only_ms": round(compute_s * 1e3, 3),
+                     "host_link_GBps": round(moved / step_s / 1e9, 2)})
+    return rows

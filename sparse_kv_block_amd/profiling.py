@@ -7,6 +7,7 @@
     python -m sparse_kv_block_amd.profiling per-kernel --fetch DIR1 --write DIR2 \
         --stats DIR3 --copy-kernel elementwise --copy-bytes N \
         --cmd-fetch "..." --cmd-write "..." --cmd-stats "..." --out profiles/X.md
+    python -m sparse_kv_block_amd.profiling pipeline BENCH.json --cmd "..." --out profiles/X.md
 
 `counters` scales the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
 what the same counters read for a plain copy kernel of known size, and records
@@ -150,6 +151,52 @@ def per_kernel(fetch_dir, write_dir, stats_dir, copy_kernel, copy_bytes, cmds, o
     return text
 
 
+def pipeline(bench_json: str, cmd: str, out: str):
+    """The 36-layer fetch-cap sweep and the host-link budget of one
+    `bench.py --pipeline --capmodel` run, as a table."""
+    with open(bench_json) as f:
+        lines = [l for l in f if l.strip().startswith("{")]
+    res = json.loads(lines[-1])
+    pl, cmod, pcie = res["pipeline_36_layer"], res["cap_model"], res["pcie"]
+    L = [f"# 36-layer decode step: fetch-cap sweep and host-link budget", "",
+         f"Command (repository root, one MI355X): `{cmd}`", "",
+         f"Kernel sources: {kernel_source_hash()}.  {pl['layers']} layers, batch {pl['batch']}, "
+         f"context {pl['ctx']}, K = {pl['k_resident']}, {pl['host_pool']}; per layer the fused "
+         "step on the main stream and the gather prefetch of its admissions on a side stream "
+         "(layer-local events).  Bytes per step from the admission counts; the bound is "
+         "layers x units x max_admit x record bytes.  Overlap fraction = (fused kernels alone + "
+         "transfer alone - step) / the shorter of the two, the transfer alone being the bytes "
+         "at the gather kernel's measured host-link rate.", "",
+         "| cap | max_admit | bytes moved / step | bound | step ms | fused kernels alone ms | "
+         "transfer alone ms | overlap fraction | host link GB/s |",
+         "|---|---|---|---|---|---|---|---|---|"]
+    for r in pl["caps"]:
+        L.append(f"| {r['cap']} | {r['max_admit']} | {r['bytes_per_step'] / 1e9:.3f} GB | "
+                 f"{r['bytes_bound'] / 1e9:.3f} GB | {r['step_ms']:.2f} | {r['compute_only_ms']:.2f} | "
+                 f"{r.get('transfer_alone_ms', float('nan')):.2f} | "
+                 f"{r.get('overlap_fraction', float('nan')):.2f} | {r['host_link_GBps']:.1f} |")
+    lk = cmod["link_GBps"]
+    L += ["", f"Host link: gather kernel {lk['gather_kernel']} GB/s "
+              f"({pcie['gather']['bytes'] / 1e6:.1f} MB of one step's admissions), one contiguous "
+              f"1 GiB SDMA copy from the pinned pool {lk['sdma_1GiB_copy']} GB/s.",
+          "Fused step: " + ", ".join(f"K = {k}: {v} us" for k, v in cmod["fused_step_us"].items())
+          + f" (window = {cmod['layers']} layers x fused step).", "",
+          "| K | link | window ms | largest max_admit that hides | cap | bytes |",
+          "|---|---|---|---|---|---|"]
+    for h in cmod["largest_hidden"]:
+        L.append(f"| {h['K']} | {h['link']} | {h['window_ms']:.2f} | {h['max_admit']} | "
+                 f"{h['cap']} | {h['bytes'] / 1e9:.3f} GB |")
+    L += ["", "| cap | max_admit | model, overlapped ms | model with the bytes moved ms | "
+              "serial ms | measured ms |", "|---|---|---|---|---|---|"]
+    for p in cmod["predicted_step_ms"]:
+        L.append(f"| {p['cap']} | {p['max_admit']} | {p['overlapped_ms']} | "
+                 f"{p['overlapped_ms_moved_bytes']} | {p['serial_ms']} | {p['measured_ms']} |")
+    text = "\n".join(L) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -178,7 +225,14 @@ def main():
     k.add_argument("--cmd-write", required=True)
     k.add_argument("--cmd-stats", required=True)
     k.add_argument("--out", required=True)
+    pp = sub.add_parser("pipeline")
+    pp.add_argument("bench_json")
+    pp.add_argument("--cmd", required=True)
+    pp.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.what == "pipeline":
+        print(pipeline(a.bench_json, a.cmd, a.out))
+        return
     if a.what == "per-kernel":
         print(per_kernel(a.fetch, a.write, a.stats, a.copy_kernel, a.copy_bytes,
                          [a.cmd_stats, a.cmd_fetch, a.cmd_write], a.out))
