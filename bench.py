@@ -221,7 +221,7 @@ def kernels_leg(cfg, layer, ctx, nbmax, qs, rec, reps: int = 10):
     byt = units * cfg.k_resident * 2 * 16 * cfg.head_dim * es + 2 * q.numel() * es
     out["lookahead_attn"] = {"us": round(us, 1), "bytes": byt, "GBps": round(byt / us / 1e3, 1)}
     us = timed(lambda: lib.score_topk(sh, q, layer.summ, layer.ctx_len, layer.topk_idx,
-                                      layer.topk_score, q_row=1))
+                                      layer.topk_score, q_row=1, workspace=layer.workspace))
     byt = sum_blocks * 2 * cfg.head_dim * es + q.numel() * es // 2 + units * cfg.k_resident * 8
     out["score_topk"] = {"us": round(us, 1), "bytes": byt, "GBps": round(byt / us / 1e3, 1)}
     saved = layer.state()

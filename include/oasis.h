@@ -151,11 +151,18 @@ oasis_status oasis_lookahead_attn(const oasis_shape* shape, const void* q,
  * (unscaled; requires min <= max as oasis_summarize produces).  Writes the
  * min(K, NB_b) best blocks in the order (score descending, block ascending)
  * to topk_idx / topk_score (fp32 score); remaining entries get -1 / -inf.
- * q_row is 1 (draft) on the per-step path, 0 (normal) for a cold start. */
+ * q_row is 1 (draft) on the per-step path, 0 (normal) for a cold start.
+ * When max_blocks exceeds 1024 the scan of a long context is split over one
+ * workgroup per 1024-block part, whose lists go to `workspace` (device
+ * memory, 256-byte aligned, at least oasis_layer_step_workspace_bytes(shape)
+ * bytes; NULL allowed when that is 0), and a second launch merges them; the
+ * result equals one scan over the whole context.  The workspace needs no
+ * initialisation; calls that may run concurrently need separate workspaces. */
 oasis_status oasis_score_topk(const oasis_shape* shape, const void* q,
                               int32_t q_row, const void* summ,
                               const int32_t* ctx_len, int32_t* topk_idx,
-                              float* topk_score, void* stream);
+                              float* topk_score, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* S4 — capped eviction at step `step` (pith.science paper page, "What
  * carries the argument": admissions per step are capped and each admitted
@@ -248,9 +255,9 @@ oasis_status oasis_topk_agreement(const oasis_shape* shape,
                                   const int32_t* l2p, int32_t exact_n,
                                   int32_t* counts, void* stream);
 
-/* Workspace bytes oasis_layer_step needs for a shape: 0 while
- * max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K lists
- * of the split summary scan). */
+/* Workspace bytes oasis_layer_step and oasis_score_topk need for a shape: 0
+ * while max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K
+ * lists of the split summary scan). */
 size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape);
 
 /* S1..S4 fused — one look-ahead layer step in one launch: attention of both

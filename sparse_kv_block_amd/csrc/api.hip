@@ -87,11 +87,27 @@ size_t esize(const oasis_shape* s) { return s->dtype == OASIS_DTYPE_F32 ? 4 : 2;
     if (!(ptr)) return fail(OASIS_ERR_INVALID, "%s: %s is NULL", fn, #ptr);     \
   } while (0)
 
+// The split-scan workspace of oasis_score_topk and oasis_layer_step: none
+// while every context fits one scan part, else at least the bytes
+// oasis_layer_step_workspace_bytes gives, 256-byte aligned.
+oasis_status check_workspace(const oasis_shape* shape, const void* workspace,
+                             size_t workspace_bytes, const char* fn) {
+  const size_t need = oasis::layer_step_workspace_bytes(to_shape(shape));
+  if (need == 0) return OASIS_OK;
+  if (!workspace) return fail(OASIS_ERR_INVALID, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(OASIS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                need);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(OASIS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+  return OASIS_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t oasis_abi_version(void) { return 7; }
+int32_t oasis_abi_version(void) { return 8; }
 
 const char* oasis_last_error(void) { return g_error.c_str(); }
 
@@ -151,7 +167,8 @@ oasis_status oasis_lookahead_attn(const oasis_shape* shape, const void* q, const
 
 oasis_status oasis_score_topk(const oasis_shape* shape, const void* q, int32_t q_row,
                               const void* summ, const int32_t* ctx_len, int32_t* topk_idx,
-                              float* topk_score, void* stream) {
+                              float* topk_score, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   const char* fn = "oasis_score_topk";
   if (oasis_status st = check_shape(shape, fn)) return st;
   if (q_row != 0 && q_row != 1) return fail(OASIS_ERR_INVALID, "%s: q_row %d (0 or 1)", fn, q_row);
@@ -161,8 +178,9 @@ oasis_status oasis_score_topk(const oasis_shape* shape, const void* q, int32_t q
   OASIS_NONNULL(ctx_len, fn);
   OASIS_NONNULL(topk_idx, fn);
   OASIS_NONNULL(topk_score, fn);
+  if (oasis_status st = check_workspace(shape, workspace, workspace_bytes, fn)) return st;
   return hip_status(oasis::launch_score_topk(to_shape(shape), shape->dtype, q, q_row, summ, ctx_len,
-                                             topk_idx, topk_score, (hipStream_t)stream),
+                                             topk_idx, topk_score, workspace, (hipStream_t)stream),
                     fn);
 }
 
@@ -352,13 +370,8 @@ oasis_status layer_step_impl(const char* fn, bool use_scratch, const oasis_shape
   OASIS_NONNULL(admit_count, fn);
   if (need > 0 && use_scratch) {
     if (oasis_status s = hip_status(oasis::scratch_pointer(&workspace), fn)) return s;
-  } else if (need > 0) {
-    OASIS_NONNULL(workspace, fn);
-    if (workspace_bytes < need)
-      return fail(OASIS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
-                  need);
-    if (((uintptr_t)workspace & 255) != 0)
-      return fail(OASIS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+  } else if (oasis_status st = check_workspace(shape, workspace, workspace_bytes, fn)) {
+    return st;
   }
   return hip_status(oasis::launch_layer_step(to_shape(shape), shape->dtype, q, pool, summ, ctx_len,
                                              scale, step, max_admit, out, topk_idx, topk_score, l2p,

@@ -152,7 +152,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// ---- split summary scan of long contexts (fused layer step) ----
+// ---- split summary scan of long contexts ----
 constexpr int kScanChunk = 1024;   // blocks per scan part
 
 struct StepWorkspace {

@@ -173,6 +173,48 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T*
   select_unit<T, D, 4, KPT>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
 }
 
+// Long contexts (NBmax above one scan part): workgroup (unit, part) scans the
+// part's kScanChunk blocks and selects their top-K.  A unit whose context fits
+// one part finishes here; otherwise the part's list goes to the workspace
+// (slot 1 + part of the unit, the layout of the fused step's split scan) and
+// split_select_kernel<false> merges the lists.  Parts past a unit's context
+// exit at once.  (512-block parts measured the same: a faster scan launch,
+// a slower merge.)
+template <typename T, int D, int U>
+__global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T* __restrict__ q,
+                                                              int q_row, const T* __restrict__ summ,
+                                                              const int32_t* __restrict__ ctx,
+                                                              int32_t* __restrict__ topk_idx,
+                                                              float* __restrict__ topk_score,
+                                                              int parts, StepWorkspace ws) {
+  extern __shared__ __align__(16) char smem[];
+  const int units = sh.B * sh.H;
+  const int unit = blockIdx.x % units;
+  const int part = blockIdx.x / units;
+  const int b = unit / sh.H, h = unit % sh.H;
+  const int nb = n_blocks(ctx[b], sh.NBmax);
+  const int np = scan_parts(nb);
+  if (part >= np) return;
+  const SelectPtrs p = select_ptrs(smem, kScanChunk, sh.K);
+  const int c0 = part * kScanChunk;
+  const int len = nb - c0 < kScanChunk ? nb - c0 : kScanChunk;
+  scan_unit<T, D, U>(sh, q, q_row, summ + ((size_t)unit * sh.NBmax + c0) * 2 * D, b, h, len,
+                     p.keys);
+  __syncthreads();
+  if (np == 1) {
+    select_from_keys<kScanChunk / kThreads>(sh, unit, len, topk_idx, topk_score, p);
+    return;
+  }
+  const int kk = topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key,
+                                                   p.cand_idx, p.cand_key, p.ev.red);
+  const size_t slot = (size_t)unit * parts + 1 + part;
+  for (int t = threadIdx.x; t < sh.K; t += kThreads) {
+    ws.key[slot * sh.K + t] = t < kk ? p.sel_key[t] : 0u;
+    ws.idx[slot * sh.K + t] = t < kk ? c0 + p.sel_idx[t] : -1;
+  }
+  if (threadIdx.x == 0) ws.n[slot] = kk;
+}
+
 // ------------------------------------------------------------------ agreement diagnostic
 // Exact block scores of one unit from its keys in the full KV, then the same
 // top-K as the summary scan's.
@@ -379,7 +421,11 @@ __host__ __device__ constexpr int attn_region(int D, int RT) {
 // Long contexts (more than kScanChunk blocks) split a unit over several
 // workgroups: part 0 runs the attention, part p >= 1 scans blocks
 // [(p-1)*kScanChunk, p*kScanChunk), selects its local top-K and publishes it
-// to the workspace.  A second kernel (split_select_kernel) then concatenates
+// to the workspace (list slot p of the unit).  (Running the attention
+// interleaved with the first part's scan, as the one-part kernel does,
+// measured slower here: the scan-only workgroups then share that kernel's
+// register budget, 2 waves per SIMD instead of 3.)  A second kernel
+// (split_select_kernel) then concatenates
 // the lists of each split unit, selects its final top-K and runs the
 // eviction; the kernel boundary orders it after the unit's attention and
 // makes the lists visible, with no device-scope fence per workgroup (on
@@ -413,6 +459,15 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
                p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
                admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+  };
+  // a scan part's list to the workspace (chunk c in slot 1 + c of the unit)
+  auto publish = [&](int kk, int c0, int chunk) {
+    const size_t slot = (size_t)unit * parts + 1 + chunk;
+    for (int t = tid; t < sh.K; t += kThreads) {
+      ws.key[slot * sh.K + t] = t < kk ? p.sel_key[t] : 0u;
+      ws.idx[slot * sh.K + t] = t < kk ? c0 + p.sel_idx[t] : -1;
+    }
+    if (tid == 0) ws.n[slot] = kk;
   };
   if constexpr (IL && kMfma) {
     // Launched only when every context fits one scan part (one workgroup per
@@ -462,12 +517,7 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
 
   if (!whole) {
     if (part == 0) return;                 // attention only
-    const size_t slot = (size_t)unit * parts + part;
-    for (int t = tid; t < sh.K; t += kThreads) {
-      ws.key[slot * sh.K + t] = t < kk ? p.sel_key[t] : 0u;
-      ws.idx[slot * sh.K + t] = t < kk ? c0 + p.sel_idx[t] : -1;
-    }
-    if (tid == 0) ws.n[slot] = kk;
+    publish(kk, c0, part - 1);
     return;                                // split_select_kernel finishes the unit
   }
   finish(kk);
@@ -477,7 +527,11 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
 // kScanChunk blocks, the scan parts' lists (each sorted by (key desc, block
 // asc), covering ascending block ranges) are concatenated in part order, so
 // equal keys stay in ascending block order and the final top-K equals that of
-// one scan over the whole context; then the capped eviction.
+// one scan over the whole context; then the capped eviction (EVICT: the fused
+// step; the standalone scan + top-K stops after the list).  (Loading the list
+// slots with the context length in one round trip, from padded lists, and
+// dropping entries below the largest K-th key of the lists measured no gain.)
+template <bool EVICT>
 __global__ __launch_bounds__(kThreads) void split_select_kernel(
     Shape sh, const int32_t* __restrict__ ctx, int step, int max_admit,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l,
@@ -485,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(
   extern __shared__ __align__(16) char smem[];
   const int unit = blockIdx.x;
   const int nb = n_blocks(ctx[unit / sh.H], sh.NBmax);
-  if (nb <= kScanChunk) return;            // finished by the step kernel
+  if (nb <= kScanChunk) return;            // finished by the scan kernel
   const int active = 1 + scan_parts(nb);
   const int tid = threadIdx.x;
   const SelectPtrs p = select_ptrs(smem, 0, sh.K);
@@ -537,10 +591,12 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(
     topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
     topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
   }
-  __syncthreads();
-  evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
-             p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
-             admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+  if constexpr (EVICT) {
+    __syncthreads();
+    evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
+               p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
+               admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+  }
 }
 
 // ------------------------------------------------------------------ dense attention
@@ -694,7 +750,28 @@ hipError_t launch_attn(const Shape& sh, int dtype, const void* q, const void* po
 
 hipError_t launch_score_topk(const Shape& sh, int dtype, const void* q, int q_row, const void* summ,
                              const int32_t* ctx, int32_t* topk_idx, float* topk_score,
-                             hipStream_t st) {
+                             void* workspace, hipStream_t st) {
+  const int parts = step_parts(sh.NBmax);
+  if (parts > 1) {
+    // split over scan parts, then merge the parts' lists
+    const StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
+    const size_t lds = SelectLds(kScanChunk, sh.K).total;
+    dim3 pgrid(sh.B * sh.H * scan_parts(sh.NBmax));
+#define OASIS_PART(T_, D_)                                                                    \
+  hipLaunchKernelGGL((score_part_kernel<T_, D_, 8>), pgrid, dim3(kThreads), lds, st, sh,      \
+                     (const T_*)q, q_row, (const T_*)summ, ctx, topk_idx, topk_score, parts, ws)
+    if (dtype == 1) { if (sh.d == 128) { OASIS_PART(uint16_t, 128); } else { OASIS_PART(uint16_t, 64); } }
+    else            { if (sh.d == 128) { OASIS_PART(float, 128); }    else { OASIS_PART(float, 64); } }
+#undef OASIS_PART
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t mlds = SelectLds(0, sh.K).total + (size_t)parts * sh.K * 8;
+    if (mlds > kMaxLds) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(split_select_kernel<false>, dim3(sh.B * sh.H), dim3(kThreads),
+                       mlds, st, sh, ctx, 0, 0, topk_idx, topk_score, nullptr, nullptr, nullptr,
+                       nullptr, nullptr, parts, ws);
+    return hipGetLastError();
+  }
   dim3 grid(sh.B * sh.H);
   const size_t lds = SelectLds(sh.NBmax, sh.K).total;
   const bool small = sh.NBmax <= 4 * kThreads;     // 4 keys per thread suffice
@@ -784,7 +861,7 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
                              int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
                              int32_t* admit_count, void* workspace, hipStream_t st) {
   const float sc = scale_or_default(scale, sh.d);
-  const int parts = step_parts(sh.NBmax);
+  const int parts = step_parts(sh.NBmax);      // list slots per unit (slot 0 unused)
   const StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
   dim3 grid(sh.B * sh.H * parts);
   const size_t sel = SelectLds(sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk, sh.K).total;
@@ -827,8 +904,8 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     if (e != hipSuccess) return e;
     const size_t lds = SelectLds(0, sh.K).total + (size_t)parts * sh.K * 8;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(split_select_kernel, dim3(sh.B * sh.H), dim3(kThreads), lds, st, sh, ctx,
-                       step, max_admit, topk_idx, topk_score, l2p, p2l, last_sel, admit,
+    hipLaunchKernelGGL(split_select_kernel<true>, dim3(sh.B * sh.H), dim3(kThreads), lds, st, sh,
+                       ctx, step, max_admit, topk_idx, topk_score, l2p, p2l, last_sel, admit,
                        admit_count, parts, ws);
   }
   return hipGetLastError();

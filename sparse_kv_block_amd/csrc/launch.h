@@ -31,7 +31,7 @@ hipError_t launch_attn(const Shape& sh, int dtype, const void* q, const void* po
                        hipStream_t st);
 hipError_t launch_score_topk(const Shape& sh, int dtype, const void* q, int q_row,
                              const void* summ, const int32_t* ctx_len, int32_t* topk_idx,
-                             float* topk_score, hipStream_t st);
+                             float* topk_score, void* workspace, hipStream_t st);
 hipError_t launch_exact_topk(const Shape& sh, int dtype, const void* q, int q_row,
                              const void* records, const int32_t* ctx_len, int32_t* topk_idx,
                              float* topk_score, hipStream_t st);

@@ -65,11 +65,13 @@ class AgreementStudy:
         L.prefetch(records, max_admit)
         lib.exact_topk(sh, q_next, records, L.ctx_len, self.exact_idx, self.exact_score, q_row=0)
         self._count("pred", L.topk_idx, L.l2p)
-        lib.score_topk(sh, q_next, L.summ, L.ctx_len, self.aux_idx, self.aux_score, q_row=0)
+        lib.score_topk(sh, q_next, L.summ, L.ctx_len, self.aux_idx, self.aux_score, q_row=0,
+                       workspace=L.workspace)
         self._count("bound", self.aux_idx)
         lib.exact_topk(sh, q, records, L.ctx_len, self.aux_idx, self.aux_score, q_row=1)
         self._count("drift", self.aux_idx)
-        lib.score_topk(sh, q, L.summ, L.ctx_len, self.aux_idx, self.aux_score, q_row=0)
+        lib.score_topk(sh, q, L.summ, L.ctx_len, self.aux_idx, self.aux_score, q_row=0,
+                       workspace=L.workspace)
         self._count("previous", self.aux_idx)
         if keep_units:
             out = {m: c.cpu().numpy().copy() for m, c in self.counts.items()}

@@ -77,7 +77,7 @@ def _load():
         "oasis_host_to_device_ptr": ([P, ctypes.POINTER(P)], I32),
         "oasis_summarize": ([SP, P, P, P, P], I32),
         "oasis_lookahead_attn": ([SP, P, P, P, P, F, P, P], I32),
-        "oasis_score_topk": ([SP, P, I32, P, P, P, P, P], I32),
+        "oasis_score_topk": ([SP, P, I32, P, P, P, P, P, ctypes.c_size_t, P], I32),
         "oasis_capped_evict": ([SP, P, I32, I32, P, P, P, P, P, P], I32),
         "oasis_prefetch": ([SP, P, P, P, P, I32, I32, P, P, P, P], I32),
         "oasis_layer_step": ([SP, P, P, P, P, F, I32, I32, P, P, P, P, P, P, P, P, P,
@@ -193,13 +193,17 @@ def lookahead_attn(shape: Shape, q, pool, p2l, ctx_len, out, scale: float = 0.0,
         _dev(out, "out", dt, qn), _stream(stream)))
 
 
-def score_topk(shape: Shape, q, summ, ctx_len, topk_idx, topk_score, q_row: int = 1, stream=None):
+def score_topk(shape: Shape, q, summ, ctx_len, topk_idx, topk_score, q_row: int = 1, stream=None,
+               workspace=None):
+    """Summary scan + top-K (see oasis_score_topk); `workspace` as for layer_step
+    (needed when max_blocks exceeds one 1024-block scan part)."""
     dt, U, K, d = shape.torch_dtype(), shape.units(), shape.k_resident, shape.head_dim
     _check(_lib.oasis_score_topk(
         ctypes.byref(shape), _dev(q, "q", dt, shape.batch * 2 * shape.n_q_heads * d), int(q_row),
         _dev(summ, "summ", dt, U * shape.max_blocks * 2 * d),
         _dev(ctx_len, "ctx_len", I32, shape.batch), _dev(topk_idx, "topk_idx", I32, U * K),
-        _dev(topk_score, "topk_score", torch.float32, U * K), _stream(stream)))
+        _dev(topk_score, "topk_score", torch.float32, U * K), *_workspace(shape, workspace),
+        _stream(stream)))
 
 
 def exact_topk(shape: Shape, q, records, ctx_len, topk_idx, topk_score, q_row: int = 0,

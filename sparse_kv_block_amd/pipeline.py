@@ -53,7 +53,8 @@ class Layer:
         self.l2p.fill_(-1)
         self.p2l.fill_(-1)
         self.last_sel.zero_()
-        lib.score_topk(self.shape, q, self.summ, self.ctx_len, self.topk_idx, self.topk_score, q_row=0)
+        lib.score_topk(self.shape, q, self.summ, self.ctx_len, self.topk_idx, self.topk_score, q_row=0,
+                       workspace=self.workspace)
         lib.capped_evict(self.shape, self.topk_idx, 0, K, self.l2p, self.p2l, self.last_sel,
                          self.admit, self.admit_count)
         self.prefetch(records, K, mode=mode, host_staging=host_staging)
@@ -89,7 +90,8 @@ class Layer:
         """The same step as four separate C-ABI calls."""
         m = self.max_admit if max_admit is None else max_admit
         lib.lookahead_attn(self.shape, q, self.pool, self.p2l, self.ctx_len, self.out, scale=scale)
-        lib.score_topk(self.shape, q, self.summ, self.ctx_len, self.topk_idx, self.topk_score, q_row=1)
+        lib.score_topk(self.shape, q, self.summ, self.ctx_len, self.topk_idx, self.topk_score, q_row=1,
+                       workspace=self.workspace)
         lib.capped_evict(self.shape, self.topk_idx, step, m, self.l2p, self.p2l, self.last_sel,
                          self.admit, self.admit_count)
 

@@ -63,7 +63,7 @@ hipError_t launch_attn(const Shape&, int, const void*, const void*, const int32_
   return hipSuccess;
 }
 hipError_t launch_score_topk(const Shape&, int, const void*, int, const void*, const int32_t*,
-                             int32_t*, float*, hipStream_t) {
+                             int32_t*, float*, void*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
@@ -154,7 +154,8 @@ static void check_shape_validation() {
     CHECK(oasis_summarize(&b.s, dummy, ctx, dummy, nullptr) == b.want);
     CHECK(strlen(oasis_last_error()) > 0);
     CHECK(oasis_lookahead_attn(&b.s, dummy, dummy, ctx, ctx, 0.f, dummy, nullptr) == b.want);
-    CHECK(oasis_score_topk(&b.s, dummy, 1, dummy, ctx, ctx, (float*)dummy, nullptr) == b.want);
+    CHECK(oasis_score_topk(&b.s, dummy, 1, dummy, ctx, ctx, (float*)dummy, nullptr, 0, nullptr) ==
+          b.want);
     CHECK(oasis_capped_evict(&b.s, ctx, 1, 1, ctx, ctx, ctx, ctx, ctx, nullptr) == b.want);
     CHECK(oasis_layer_step(&b.s, dummy, dummy, dummy, ctx, 0.f, 1, 1, dummy, ctx, (float*)dummy,
                            ctx, ctx, ctx, ctx, ctx, nullptr, 0, nullptr) == b.want);
@@ -173,8 +174,8 @@ static void check_null_arguments() {
   CHECK(oasis_summarize(&s, d, nullptr, d, nullptr) == OASIS_ERR_INVALID);
   CHECK(oasis_lookahead_attn(&s, d, d, nullptr, c, 0.f, d, nullptr) == OASIS_ERR_INVALID);
   CHECK(oasis_lookahead_attn(&s, d, d, c, c, 1.f / 0.f, d, nullptr) == OASIS_ERR_INVALID);
-  CHECK(oasis_score_topk(&s, d, 2, d, c, c, f, nullptr) == OASIS_ERR_INVALID);
-  CHECK(oasis_score_topk(&s, d, 1, d, c, nullptr, f, nullptr) == OASIS_ERR_INVALID);
+  CHECK(oasis_score_topk(&s, d, 2, d, c, c, f, nullptr, 0, nullptr) == OASIS_ERR_INVALID);
+  CHECK(oasis_score_topk(&s, d, 1, d, c, nullptr, f, nullptr, 0, nullptr) == OASIS_ERR_INVALID);
   CHECK(oasis_capped_evict(&s, c, 1, -1, c, c, c, c, c, nullptr) == OASIS_ERR_INVALID);
   CHECK(oasis_capped_evict(&s, c, 1, 1, c, c, nullptr, c, c, nullptr) == OASIS_ERR_INVALID);
   CHECK(oasis_append_token(&s, d, d, d, d, nullptr, d, c, nullptr) == OASIS_ERR_INVALID);
@@ -223,8 +224,14 @@ static void check_layer_step_workspace() {
   CHECK(oasis_layer_step(&s, d, d, d, c, 0.f, 1, 6, d, c, f, c, c, c, c, c, aligned, need,
                          nullptr) == OASIS_OK);
   CHECK(g_launches == before + 1);
+  // the standalone scan + top-K takes the same workspace
+  CHECK(oasis_score_topk(&s, d, 1, d, c, c, f, nullptr, need, nullptr) == OASIS_ERR_INVALID);
+  CHECK(oasis_score_topk(&s, d, 1, d, c, c, f, aligned, need - 1, nullptr) == OASIS_ERR_INVALID);
+  CHECK(oasis_score_topk(&s, d, 1, d, c, c, f, aligned + 16, need, nullptr) == OASIS_ERR_INVALID);
+  CHECK(oasis_score_topk(&s, d, 1, d, c, c, f, aligned, need, nullptr) == OASIS_OK);
   s.max_blocks = 1024;                            // one scan part: no workspace
   CHECK(oasis_layer_step_workspace_bytes(&s) == 0);
+  CHECK(oasis_score_topk(&s, d, 1, d, c, c, f, nullptr, 0, nullptr) == OASIS_OK);
   CHECK(oasis_layer_step(&s, d, d, d, c, 0.f, 1, 6, d, c, f, c, c, c, c, c, nullptr, 0, nullptr) ==
         OASIS_OK);
 }

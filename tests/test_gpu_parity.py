@@ -110,7 +110,7 @@ def test_score_topk_gaussian(case, q_row):
     layer = Layer(cfg, ctx, nbmax)
     layer.summarize(rec)
     lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score,
-                   q_row=q_row)
+                   q_row=q_row, workspace=layer.workspace)
     summ = oracle.summarize(rec.cpu(), ctx, 16)
     sc = oracle.block_scores(q.cpu(), summ, ctx, 16, q_row=q_row)
     idx, _ = oracle.topk(sc, ctx, 16, cfg.k_resident)
@@ -126,7 +126,8 @@ def test_score_topk_exact_on_integer_inputs(case):
     ctx, nbmax, rec, q = setup(cfg, ctx, seed=4, integer=True)
     layer = Layer(cfg, ctx, nbmax)
     layer.summarize(rec)
-    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score,
+                   workspace=layer.workspace)
     summ = oracle.summarize(rec.cpu(), ctx, 16)
     sc = oracle.block_scores(q.cpu(), summ, ctx, 16)
     idx, val = oracle.topk(sc, ctx, 16, cfg.k_resident)
@@ -140,11 +141,36 @@ def test_topk_with_more_slots_than_blocks_and_large_context():
     ctx, nbmax, rec, q = setup(cfg, [131072, 100, 3200], seed=5)
     layer = Layer(cfg, ctx, nbmax)
     layer.summarize(rec)
-    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score,
+                   workspace=layer.workspace)
     summ = oracle.summarize(rec.cpu(), ctx, 16)
     sc = oracle.block_scores(q.cpu(), summ, ctx, 16)
     idx, _ = oracle.topk(sc, ctx, 16, cfg.k_resident)
     check_topk(i32(layer.topk_idx), host(layer.topk_score), idx, sc, what="large")
+
+
+@pytest.mark.parametrize("dtype,K,d", [("bf16", 1, 128), ("bf16", 37, 64), ("bf16", 128, 128),
+                                       ("bf16", 256, 128), ("f32", 128, 64)])
+def test_score_topk_split_over_scan_parts_exact_on_integer_inputs(dtype, K, d):
+    # contexts past 1024 blocks: one workgroup per 1024-block part, then a
+    # merge launch; contexts on and around the part boundaries, one that fits
+    # a single part (finished by its part workgroup) and an empty request
+    cfg = small(dtype=dtype, batch=7, k_resident=K, head_dim=d, n_q_heads=8, n_kv_heads=2,
+                planted=0)
+    ctx = [16 * 1024, 16 * 1024 + 1, 16 * 2048 + 15, 16 * 5000 - 3, 700, 0, 131072]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=21, integer=True)
+    layer = Layer(cfg, ctx, nbmax)
+    assert layer.workspace is not None
+    layer.summarize(rec)
+    for q_row in (0, 1):
+        layer.topk_idx.fill_(-7)
+        lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score,
+                       q_row=q_row, workspace=layer.workspace)
+        summ = oracle.summarize(rec.cpu(), ctx, 16)
+        sc = oracle.block_scores(q.cpu(), summ, ctx, 16, q_row=q_row)
+        idx, val = oracle.topk(sc, ctx, 16, K)
+        np.testing.assert_array_equal(i32(layer.topk_idx), idx)
+        np.testing.assert_array_equal(host(layer.topk_score).astype(np.float64), val)
 
 
 def designed_scores(nb: int, pattern: int) -> np.ndarray:
@@ -201,7 +227,8 @@ def test_topk_designed_key_distributions(dtype, K):
     idx, val = oracle.topk(sc, ctx, 16, K)
     layer = Layer(cfg, ctx, nbmax)
     layer.summarize(rec)
-    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score,
+                   workspace=layer.workspace)
     np.testing.assert_array_equal(i32(layer.topk_idx), idx)
     np.testing.assert_array_equal(host(layer.topk_score).astype(np.float64), val)
     layer.cold_fill(q, rec)
