@@ -344,42 +344,78 @@ __device__ __forceinline__ void attn_unit_bf16(const Shape& sh, const uint16_t* 
 
 // fp32 look-ahead attention: one wave per query row, 64 tokens (4 slots) per
 // step, online softmax in fp32.
+// LDS floats the fp32 path needs: per wave one query row and 64 weights.
+__host__ __device__ constexpr int attn_f32_lds_bytes(int D) { return kWaves * (D + kWave) * 4; }
+
+// fp32 path: one wave per stacked row; per group of four slots (64 tokens,
+// one per lane) every key row and value column of the group is loaded at once
+// (the loads do not wait on each other), the row's query and the 64 weights
+// are broadcast through LDS, and the online softmax runs over the group.
+// `lds`: attn_f32_lds_bytes(D) bytes.
 template <int D>
 __device__ __forceinline__ void attn_unit_f32(const Shape& sh, const float* __restrict__ q,
                                               const float* __restrict__ pool,
                                               const int32_t* __restrict__ p2l, int b, int h,
-                                              int L, float scale, float* __restrict__ out) {
+                                              int L, float scale, float* __restrict__ out,
+                                              float* lds) {
   constexpr int REC = 2 * kBlock * D;
-  constexpr int CPL = (D + kWave - 1) / kWave;
+  constexpr int CPL = D / kWave;          // output channels per lane
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int lane = tid % kWave;
   const int G = sh.G;
+  const int K = sh.K;
   const int unit = b * sh.H + h;
-  const float* unit_pool = pool + (size_t)unit * sh.K * REC;
+  const float* unit_pool = pool + (size_t)unit * K * REC;
+  float* qs = lds + w * (D + kWave);      // this wave's query row
+  float* ps = qs + D;                     // the group's 64 weights
+  const int32_t* slots = p2l + (size_t)unit * K;
   for (int r = w; r < 2 * G; r += kWaves) {
     const int row = r < G ? 0 : 1;
     const int head = h * G + (r < G ? r : r - G);
     const float* qr = q + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) qs[lane + kWave * i] = qr[lane + kWave * i];
     float m = -INFINITY, lsum = 0.f;
     float acc[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-    for (int sb = 0; sb < sh.K; sb += 4) {
+    for (int sb = 0; sb < K; sb += 4) {
+      // lane = token u of slot sb + lane / 16
       const int s = sb + lane / kBlock;
       const int u = lane % kBlock;
-      int j = -1;
-      if (s < sh.K) j = p2l[(size_t)unit * sh.K + s];
-      const bool valid = s < sh.K && j >= 0 && j < sh.NBmax && j * kBlock + u < L;
-      float z = -INFINITY;
-      if (valid) {
-        const float* kr = unit_pool + (size_t)s * REC + u * D;
-        float dot = 0.f;
-        for (int c = 0; c < D; ++c) dot = fmaf(qr[c], kr[c], dot);
-        z = dot * scale;
+      const int sc = s < K ? s : K - 1;                 // clamped, masked below
+      const int j = slots[sc];
+      const bool valid = s < K && j >= 0 && j < sh.NBmax && j * kBlock + u < L;
+      const f32x4* kr = reinterpret_cast<const f32x4*>(unit_pool + (size_t)sc * REC + u * D);
+      f32x4 kv[D / 4];
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) kv[i] = kr[i];
+      // value columns of the group's four slots for this lane's channels
+      f32x4 vv[CPL][4][4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int sq = sb + qq < K ? sb + qq : K - 1;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const f32x4* vc = reinterpret_cast<const f32x4*>(
+              unit_pool + (size_t)sq * REC + kBlock * D + (lane + kWave * i) * kBlock);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[i][qq][e] = vc[e];
+        }
       }
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) {
+        const f32x4 q4 = reinterpret_cast<const f32x4*>(qs)[i];
+        dot = fmaf(q4[0], kv[i][0], dot);
+        dot = fmaf(q4[1], kv[i][1], dot);
+        dot = fmaf(q4[2], kv[i][2], dot);
+        dot = fmaf(q4[3], kv[i][3], dot);
+      }
+      const float z = valid ? dot * scale : -INFINITY;
       const float cm = wave_max(z);
-      if (cm == -INFINITY) continue;
+      if (cm == -INFINITY) continue;                     // uniform across the wave
       const float nm = fmaxf(m, cm);
       const float f = (m == -INFINITY) ? 0.f : expf(m - nm);
       m = nm;
@@ -388,24 +424,27 @@ __device__ __forceinline__ void attn_unit_f32(const Shape& sh, const float* __re
       for (int i = 0; i < CPL; ++i) acc[i] *= f;
       const float p = valid ? expf(z - m) : 0.f;
       lsum += wave_sum(p);
-      for (int t = 0; t < kWave; ++t) {
-        const float pt = __shfl(p, t);
-        if (pt == 0.f) continue;
-        const int st = sb + t / kBlock, ut = t % kBlock;
-        const float* vr = unit_pool + (size_t)st * REC + kBlock * D;
+      ps[lane] = p;
+      // values of tokens outside the resident set or the context never enter
+      // the sum (whatever the pool holds there)
+      const uint64_t vmask = ballot(valid);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          const int c = lane + kWave * i;
-          if (c < D) acc[i] = fmaf(pt, vr[c * kBlock + ut], acc[i]);
+      for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4 p4 = reinterpret_cast<const f32x4*>(ps)[4 * qq + e];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const bool in = (vmask >> (16 * qq + 4 * e + k)) & 1ull;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc[i] = fmaf(p4[k], in ? vv[i][qq][e][k] : 0.f, acc[i]);
+          }
         }
       }
     }
     float* orow = out + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = lane + kWave * i;
-      if (c < D) orow[c] = lsum > 0.f ? acc[i] / lsum : 0.f;
-    }
+    for (int i = 0; i < CPL; ++i) orow[lane + kWave * i] = lsum > 0.f ? acc[i] / lsum : 0.f;
   }
 }
 

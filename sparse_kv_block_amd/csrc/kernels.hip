@@ -97,9 +97,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(Shape sh, const floa
                                                             const int32_t* __restrict__ p2l,
                                                             const int32_t* __restrict__ ctx,
                                                             float scale, float* __restrict__ out) {
+  extern __shared__ __align__(16) char smem[];
   const int unit = blockIdx.x;
   const int b = unit / sh.H, h = unit % sh.H;
-  attn_unit_f32<D>(sh, q, pool, p2l, b, h, ctx[b], scale, out);
+  attn_unit_f32<D>(sh, q, pool, p2l, b, h, ctx[b], scale, out, reinterpret_cast<float*>(smem));
 }
 
 // ------------------------------------------------------------------ scan + top-K
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   const int part = blockIdx.x / units;
   const int b = unit / sh.H, h = unit % sh.H;
   const int tid = threadIdx.x;
-  const int attn_bytes = kMfma ? attn_region(D, RT) : 0;
+  const int attn_bytes = kMfma ? attn_region(D, RT) : attn_f32_lds_bytes(D);
   const SelectPtrs p = select_ptrs(smem + attn_bytes, sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk,
                                    sh.K);
   // the unit's top-K list out, then the capped eviction (kk = list length)
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     if constexpr (kMfma)
       attn_unit_bf16<D, RT>(sh, q, pool, p2l, b, h, L, scale, out, reinterpret_cast<float*>(smem));
     else
-      attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out);
+      attn_unit_f32<D>(sh, q, pool, p2l, b, h, L, scale, out, reinterpret_cast<float*>(smem));
   };
   auto scan_select = [&]() -> int {
     scan_unit<T, D, U>(sh, q, 1, summ + ((size_t)unit * sh.NBmax + c0) * 2 * D, b, h, len, p.keys);
@@ -739,10 +740,10 @@ hipError_t launch_attn(const Shape& sh, int dtype, const void* q, const void* po
 #undef OASIS_ATTN
   } else {
     if (sh.d == 128)
-      hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(kThreads), 0, st, sh,
+      hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(kThreads), attn_f32_lds_bytes(128), st, sh,
                          (const float*)q, (const float*)pool, p2l, ctx, sc, (float*)out);
     else
-      hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(kThreads), 0, st, sh,
+      hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(kThreads), attn_f32_lds_bytes(64), st, sh,
                          (const float*)q, (const float*)pool, p2l, ctx, sc, (float*)out);
   }
   return hipGetLastError();
@@ -889,7 +890,7 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     }
 #undef OASIS_STEP
   } else {
-    const size_t lds = sel;
+    const size_t lds = attn_f32_lds_bytes(sh.d) + sel;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
 #define OASIS_STEP32(D_)                                                                        \
   hipLaunchKernelGGL((layer_step_kernel<float, D_, 1, 4, false>), grid, dim3(kThreads), lds, st, sh,    \
