@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from parity import host, i32, pool_from_records, sample_units, unit_slice
+from parity import host, i32, pool_from_records
 from sparse_kv_block_amd import gen
 from sparse_kv_block_amd.configs import QWEN3_8B_16K, Config
 
@@ -126,17 +126,18 @@ def test_append_matches_oracle(case, where, with_pool):
 
 
 def test_append_full_size_qwen3_8b_16k():
-    """One append at the 128-request, 8-KV-head, 16K-context shape, checked on
-    sampled units (records, resident copies and summaries of the touched
-    block) and on every request's context length."""
+    """One append at the 128-request, 8-KV-head, 16K-context shape, every unit
+    against the oracle: the touched block record of every unit, the whole
+    resident pool (the tail block made resident in every other unit) and every
+    summary, and every request's context length."""
     cfg = QWEN3_8B_16K
     ctx = gen.context_lengths(cfg)
     nbmax = cfg.max_blocks(int(ctx.max())) + 1
     say(f"append full size: B={cfg.batch} NBmax={nbmax}")
     rec = gen.records(cfg, ctx, nbmax, device=DEV)
     l2p, p2l, _ = gen.random_state(cfg, ctx, nbmax, seed=6)
-    units = sample_units(cfg.batch, cfg.n_kv_heads, 8, cfg.seed + 1)
-    make_tail_resident(l2p, p2l, ctx, units[::2])
+    every_other = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_kv_heads) if (b + h) % 2 == 0]
+    make_tail_resident(l2p, p2l, ctx, every_other)
     l2p, p2l = l2p.to(DEV), p2l.to(DEV)
     pool = pool_from_records(rec, p2l)
     shape = lib.Shape.of(cfg, nbmax)
@@ -146,19 +147,15 @@ def test_append_full_size_qwen3_8b_16k():
     lib.summarize(shape, rec, ctx_g, summ)
     kn, vn = gen.new_tokens(cfg, 1, seed=12, device=DEV)
     torch.cuda.synchronize()
-    before = {u: (unit_slice(rec, *u, cfg.group, "unit").cpu(),
-                  unit_slice(pool, *u, cfg.group, "unit").cpu(),
-                  unit_slice(summ, *u, cfg.group, "unit").cpu()) for u in units}
+    r_o, p_o, s_o = (oracle.as_np(x.cpu()).copy() for x in (rec, pool, summ))
+    c_o = ctx.copy()
     lib.append_token(shape, kn[0], vn[0], rec, summ, ctx_g, pool=pool, l2p=l2p)
     torch.cuda.synchronize()
-    assert i32(ctx_g).tolist() == (ctx + 1).tolist()
-    for (b, h) in units:
-        r, p, s = (oracle.as_np(x).copy() for x in before[(b, h)])
-        c = ctx[b:b + 1].copy()
-        oracle.append(kn[0, b:b + 1, h:h + 1].cpu(), vn[0, b:b + 1, h:h + 1].cpu(), r, s, c, 16,
-                      pool=p, l2p=l2p[b:b + 1, h:h + 1].cpu().numpy())
-        j = int(ctx[b]) // 16
-        np.testing.assert_array_equal(oracle.as_np(rec[b, h, j].cpu()), r[0, 0, j])
-        np.testing.assert_array_equal(oracle.as_np(pool[b:b + 1, h:h + 1].cpu()), p)
-        np.testing.assert_array_equal(oracle.to_f64(host(summ[b:b + 1, h:h + 1, j])),
-                                      oracle.to_f64(s[:, :, j]))
+    oracle.append(kn[0].cpu(), vn[0].cpu(), r_o, s_o, c_o, 16, pool=p_o, l2p=i32(l2p))
+    np.testing.assert_array_equal(i32(ctx_g), c_o)
+    assert c_o.tolist() == (ctx + 1).tolist()
+    j = torch.from_numpy(ctx.astype(np.int64) // 16).to(DEV)
+    touched = rec[torch.arange(cfg.batch, device=DEV), :, j]          # [B][Hkv][record]
+    np.testing.assert_array_equal(host(touched), r_o[np.arange(cfg.batch), :, ctx // 16])
+    np.testing.assert_array_equal(host(pool), p_o)
+    np.testing.assert_array_equal(oracle.to_f64(host(summ)), oracle.to_f64(s_o))
