@@ -155,9 +155,11 @@ oasis_status oasis_lookahead_attn(const oasis_shape* shape, const void* q,
  * When max_blocks exceeds 1024 the scan of a long context is split over one
  * workgroup per 1024-block part, whose lists go to `workspace` (device
  * memory, 256-byte aligned, at least oasis_layer_step_workspace_bytes(shape)
- * bytes; NULL allowed when that is 0), and a second launch merges them; the
- * result equals one scan over the whole context.  The workspace needs no
- * initialisation; calls that may run concurrently need separate workspaces. */
+ * bytes; NULL allowed when that is 0); the last of a unit's parts to finish
+ * merges them (one launch), and the result equals one scan over the whole
+ * context.  The workspace needs no initialisation (its per-unit arrival
+ * words carry a per-launch tag, so earlier contents count as zero); calls
+ * that may run concurrently need separate workspaces. */
 oasis_status oasis_score_topk(const oasis_shape* shape, const void* q,
                               int32_t q_row, const void* summ,
                               const int32_t* ctx_len, int32_t* topk_idx,
@@ -257,7 +259,7 @@ oasis_status oasis_topk_agreement(const oasis_shape* shape,
 
 /* Workspace bytes oasis_layer_step and oasis_score_topk need for a shape: 0
  * while max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K
- * lists of the split summary scan). */
+ * lists of the split summary scan and one 8-byte arrival word). */
 size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape);
 
 /* S1..S4 fused — one look-ahead layer step in one launch: attention of both
@@ -268,9 +270,10 @@ size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape);
  * of a long context is split over several workgroups whose partial top-K
  * lists go to `workspace` (device memory, 256-byte aligned, at least
  * oasis_layer_step_workspace_bytes(shape) bytes; NULL allowed when that is
- * 0), and a second launch merges them and runs the eviction.  The workspace
- * needs no initialisation; calls that may run concurrently need separate
- * workspaces. */
+ * 0); the last of the unit's workgroups to finish (the attention's
+ * included) merges them and runs the eviction, all in one launch.  The
+ * workspace needs no initialisation (as for oasis_score_topk); calls that may
+ * run concurrently need separate workspaces. */
 oasis_status oasis_layer_step(const oasis_shape* shape, const void* q,
                               const void* pool, const void* summ,
                               const int32_t* ctx_len, float scale,
@@ -283,7 +286,7 @@ oasis_status oasis_layer_step(const oasis_shape* shape, const void* q,
 
 /* The fused step for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
- * the same launches and results as oasis_layer_step, with the split-scan
+ * the same launch and results as oasis_layer_step, with the split-scan
  * lists kept in the library's own device scratch instead of a workspace
  * argument.  The scratch is a 32 MiB array per device, held from the first
  * call on that device until the process ends; shapes whose lists exceed it

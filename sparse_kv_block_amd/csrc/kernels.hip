@@ -2,10 +2,12 @@
 //
 // Every per-unit kernel runs one 256-thread workgroup per (request, KV head):
 // the units are independent (their blocks, summaries, maps and slots are
-// disjoint), so nothing crosses workgroups and the launch needs no inter-block
-// synchronisation.  At batch 128 x 8 KV heads that is 1024 workgroups; the
+// disjoint).  Only a long context's split over several workgroups hands data
+// from one workgroup to another (the scan parts' lists, merged by the last of
+// the unit's workgroups to finish).  At batch 128 x 8 KV heads that is 1024 workgroups; the
 // fused step's register use (about 220 VGPRs, two waves per SIMD) places two
 // per CU, so they run in two even rounds over the 256 CUs.
+#include <atomic>
 #include <mutex>
 
 #include "attn_dev.h"
@@ -174,12 +176,210 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Shape sh, const T*
   select_unit<T, D, 4, KPT>(sh, q, q_row, summ, unit, ctx[unit / sh.H], topk_idx, topk_score, p);
 }
 
+// ---- hand-over of a split unit's lists inside one launch ----
+// A scan part's list goes to the workspace with device-coherent stores, and
+// the unit's workgroups then count their arrivals on a per-unit word; the
+// last one to arrive merges the lists (and, in the fused step, runs the
+// eviction).  The lists are read back with device-coherent loads, so no
+// device-scope fence is needed: on gfx950 such a fence writes back or
+// invalidates a whole XCD's L2 and costs more than the merge launch it would
+// save.  The arrival word holds this launch's tag in bits 16..63 and the count
+// in bits 0..15; a word with another tag (an earlier launch, or memory never
+// written by one) counts as zero, and the last arrival leaves the count at
+// zero, so the workspace needs no initialisation and a replayed launch (same
+// tag) starts from zero as well.
+template <typename V>
+__device__ __forceinline__ void ws_store(V* ptr, V v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool COHERENT, typename V>
+__device__ __forceinline__ V ws_load(const V* ptr) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(const_cast<V*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *ptr;
+}
+
+// A scan part's list (slot 1 + part of the unit): blocks c0 + local index.
+__device__ __forceinline__ void publish_list(const Shape& sh, const StepWorkspace& ws, int unit,
+                                             int parts, int part, int c0, int kk,
+                                             const SelectPtrs& p) {
+  const size_t slot = (size_t)unit * parts + 1 + part;
+  for (int t = threadIdx.x; t < sh.K; t += kThreads) {
+    ws_store(&ws.key[slot * sh.K + t], t < kk ? p.sel_key[t] : 0u);
+    ws_store(&ws.idx[slot * sh.K + t], t < kk ? c0 + p.sel_idx[t] : -1);
+  }
+  if (threadIdx.x == 0) ws_store(&ws.n[slot], kk);
+}
+
+// Called by every thread of each of the unit's `total` workgroups once its
+// stores to the workspace are issued; true in the last one to arrive.
+__device__ __forceinline__ bool arrive_last(const StepWorkspace& ws, int unit, int total,
+                                            int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);           // this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long* w = ws.arrive + unit;
+    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int c;
+    for (;;) {                             // ends: a failed exchange means another arrival
+      c = (old >> 16) == (ws.tag >> 16) ? (int)(old & 0xffffu) : 0;
+      const unsigned long long nw = c + 1 == total ? ws.tag : (ws.tag | (unsigned)(c + 1));
+      if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    *flag = c + 1 == total;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// LDS for the concatenated lists of a merge (keys, then block indices).
+__host__ __device__ inline int merge_lds_bytes(int parts, int K) {
+  return parts > 1 ? (((parts - 1) * K * 8 + 15) & ~15) : 0;
+}
+
+// The merge of a split unit's np lists (each sorted by (key desc, block asc),
+// covering ascending block ranges): concatenated in part order, so equal keys
+// stay in ascending block order and the final top-K equals that of one scan
+// over the whole context; then the list out and (EVICT) the capped eviction.
+// COHERENT: the lists were written in the same launch.
+template <bool EVICT, bool COHERENT>
+__device__ void merge_unit(const Shape& sh, int unit, int np, int step, int max_admit,
+                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_score,
+                           int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                           int32_t* admit_count, int parts, const StepWorkspace& ws,
+                           const SelectPtrs& p, char* merge_lds) {
+  const int tid = threadIdx.x;
+  uint32_t* mkey = reinterpret_cast<uint32_t*>(merge_lds);
+  int* midx = reinterpret_cast<int*>(mkey + (parts - 1) * sh.K);
+  // every part's length, then all entries in one pass (entries past a list's
+  // length are not stored).  (Issuing the entry loads with the lengths, in one
+  // round trip, measured slower: the registers they hold.)
+  int* lens = p.ev.red;                       // the eviction's counters are free here
+  if (tid < np) {
+    const int n = ws_load<COHERENT>(&ws.n[(size_t)unit * parts + 1 + tid]);
+    lens[tid] = n < 0 ? 0 : (n > sh.K ? sh.K : n);
+  }
+  __syncthreads();
+  int total = 0;
+  for (int pp = 0; pp < np; ++pp) total += lens[pp];
+  for (int e = tid; e < np * sh.K; e += kThreads) {
+    const int pp = e / sh.K, r = e % sh.K;
+    const size_t sl = (size_t)unit * parts + 1 + pp;
+    const uint32_t k = ws_load<COHERENT>(&ws.key[sl * sh.K + r]);
+    const int i = ws_load<COHERENT>(&ws.idx[sl * sh.K + r]);
+    int off = 0;
+    for (int x = 0; x < pp; ++x) off += lens[x];
+    if (r < lens[pp]) {
+      mkey[off + r] = k;
+      midx[off + r] = i;
+    }
+  }
+  __syncthreads();
+  // at most 8192 / kScanChunk lists of K <= 256 entries; keys per thread
+  // sized to the unit's list total (the selection's passes run over every
+  // register slot, filled or not; the result does not depend on the count)
+  constexpr int kMergeKpt = (8192 / kScanChunk) * 256 / kThreads;
+  int kk;
+  if (total <= kThreads)
+    kk = topk_unit<1>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  else if (total <= 2 * kThreads)
+    kk = topk_unit<2>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  else if (total <= 4 * kThreads)
+    kk = topk_unit<4>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+  else
+    kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key,
+                              p.ev.red);
+  for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
+  __syncthreads();
+  for (int t = tid; t < sh.K; t += kThreads) {
+    if (t >= kk) p.sel_idx[t] = -1;
+    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
+    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
+  }
+  if constexpr (EVICT) {
+    __syncthreads();
+    evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
+               p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
+               admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
+  }
+}
+
+// Order of the scan workgroups of a launch whose contexts differ in length:
+// workgroups start roughly in index order, so the launch should end on its
+// shortest work.  Item j (0-based) maps to (unit, scan part sp): first every
+// full kScanChunk-block part (part 0 of every unit that has one, then part 1,
+// ...), then the shorter last parts, longest first (in 128-block bands, each
+// in request order), every request's heads together.  SINGLE: units whose
+// context fits one part have a scan item too (the standalone scan); without
+// it they have none (the fused step scans them with the attention).
+// Returns false past the last item.  Every wave computes the same result:
+// one ballot per group and 64 requests, twice.
+template <bool SINGLE>
+__device__ bool scan_item(const Shape& sh, const int32_t* __restrict__ ctx, int j, int& unit,
+                          int& sp) {
+  constexpr int kFull = 8192 / kScanChunk;       // groups of full parts
+  constexpr int kBands = kScanChunk / 128;       // groups of last parts
+  const int lane = threadIdx.x & (kWave - 1);
+  int full = 0, band = -1, np = 0;
+  auto info = [&](int bb) {
+    const int nb = bb < sh.B ? n_blocks(ctx[bb], sh.NBmax) : -1;
+    np = nb < 0 ? 0 : (nb > kScanChunk ? (nb + kScanChunk - 1) / kScanChunk : (SINGLE ? 1 : 0));
+    const int rem = np > 0 ? nb - (np - 1) * kScanChunk : 0;     // blocks of the last part
+    full = rem == kScanChunk ? np : (np > 0 ? np - 1 : 0);
+    band = (np > 0 && rem < kScanChunk) ? kBands - 1 - (rem > 0 ? (rem - 1) / 128 : 0) : -1;
+  };
+  int cnt[kFull + kBands];
+#pragma unroll
+  for (int g = 0; g < kFull + kBands; ++g) cnt[g] = 0;
+  for (int c0 = 0; c0 < sh.B; c0 += kWave) {
+    info(c0 + lane);
+#pragma unroll
+    for (int g = 0; g < kFull; ++g) cnt[g] += __builtin_popcountll(ballot(full > g));
+#pragma unroll
+    for (int q = 0; q < kBands; ++q) cnt[kFull + q] += __builtin_popcountll(ballot(band == q));
+  }
+  int g = kFull + kBands, k = j;           // (static indices keep cnt in registers)
+#pragma unroll
+  for (int x = 0; x < kFull + kBands; ++x) {
+    const int n = cnt[x] * sh.H;
+    if (g == kFull + kBands) {
+      if (k < n) g = x;
+      else k -= n;
+    }
+  }
+  if (g == kFull + kBands) return false;
+  const int h = k % sh.H;
+  k /= sh.H;
+  for (int c0 = 0; c0 < sh.B; c0 += kWave) {
+    info(c0 + lane);
+    const bool in = g < kFull ? full > g : band == g - kFull;
+    const uint64_t m = ballot(in);
+    const int c = __builtin_popcountll(m);
+    if (k < c) {
+      const uint64_t pick = ballot(in && lanes_below(m) == k);
+      const int l = __builtin_ctzll(pick);
+      unit = (c0 + l) * sh.H + h;
+      sp = g < kFull ? g : __builtin_amdgcn_readlane(np, l) - 1;
+      return true;
+    }
+    k -= c;
+  }
+  return false;
+}
+
+// Requests up to which the launches take the ordered mapping above (every
+// workgroup reads all context lengths once).
+constexpr int kOrderedMaxBatch = 256;
+
 // Long contexts (NBmax above one scan part): workgroup (unit, part) scans the
 // part's kScanChunk blocks and selects their top-K.  A unit whose context fits
 // one part finishes here; otherwise the part's list goes to the workspace
 // (slot 1 + part of the unit, the layout of the fused step's split scan) and
-// split_select_kernel<false> merges the lists.  Parts past a unit's context
-// exit at once.  (512-block parts measured the same: a faster scan launch,
+// the unit's last part to finish merges the lists.  Parts past a unit's
+// context exit at once.  (512-block parts measured the same: a faster scan,
 // a slower merge.)
 template <typename T, int D, int U>
 __global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T* __restrict__ q,
@@ -187,16 +387,20 @@ __global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T*
                                                               const int32_t* __restrict__ ctx,
                                                               int32_t* __restrict__ topk_idx,
                                                               float* __restrict__ topk_score,
-                                                              int parts, StepWorkspace ws) {
+                                                              int parts, bool ordered,
+                                                              StepWorkspace ws) {
   extern __shared__ __align__(16) char smem[];
   const int units = sh.B * sh.H;
-  const int unit = blockIdx.x % units;
-  const int part = blockIdx.x / units;
+  int unit = blockIdx.x % units;
+  int part = blockIdx.x / units;
+  if (ordered && !scan_item<true>(sh, ctx, blockIdx.x, unit, part)) return;
   const int b = unit / sh.H, h = unit % sh.H;
   const int nb = n_blocks(ctx[b], sh.NBmax);
   const int np = scan_parts(nb);
   if (part >= np) return;
-  const SelectPtrs p = select_ptrs(smem, kScanChunk, sh.K);
+  __shared__ int last;
+  const int head = merge_lds_bytes(parts, sh.K);
+  const SelectPtrs p = select_ptrs(smem + head, kScanChunk, sh.K);
   const int c0 = part * kScanChunk;
   const int len = nb - c0 < kScanChunk ? nb - c0 : kScanChunk;
   scan_unit<T, D, U>(sh, q, q_row, summ + ((size_t)unit * sh.NBmax + c0) * 2 * D, b, h, len,
@@ -208,12 +412,10 @@ __global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T*
   }
   const int kk = topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key,
                                                    p.cand_idx, p.cand_key, p.ev.red);
-  const size_t slot = (size_t)unit * parts + 1 + part;
-  for (int t = threadIdx.x; t < sh.K; t += kThreads) {
-    ws.key[slot * sh.K + t] = t < kk ? p.sel_key[t] : 0u;
-    ws.idx[slot * sh.K + t] = t < kk ? c0 + p.sel_idx[t] : -1;
-  }
-  if (threadIdx.x == 0) ws.n[slot] = kk;
+  publish_list(sh, ws, unit, parts, part, c0, kk, p);
+  if (!arrive_last(ws, unit, np, &last)) return;
+  merge_unit<false, true>(sh, unit, np, 0, 0, topk_idx, topk_score, nullptr, nullptr, nullptr,
+                          nullptr, nullptr, parts, ws, p, smem);
 }
 
 // ------------------------------------------------------------------ agreement diagnostic
@@ -425,28 +627,37 @@ __host__ __device__ constexpr int attn_region(int D, int RT) {
 // to the workspace (list slot p of the unit).  (Running the attention
 // interleaved with the first part's scan, as the one-part kernel does,
 // measured slower here: the scan-only workgroups then share that kernel's
-// register budget, 2 waves per SIMD instead of 3.)  A second kernel
-// (split_select_kernel) then concatenates
-// the lists of each split unit, selects its final top-K and runs the
-// eviction; the kernel boundary orders it after the unit's attention and
-// makes the lists visible, with no device-scope fence per workgroup (on
-// gfx950 such a fence writes back or invalidates an XCD's whole L2, which
-// cost more than the scan itself).
+// register budget, 2 waves per SIMD instead of 3.)  All of the unit's
+// workgroups, the attention's included, then count their arrivals; the last
+// merges the lists and runs the eviction, which so comes after the unit's
+// attention has read the slot map.
+
+// LDS before the select area: the attention merge area, which also holds a
+// split unit's concatenated lists once the attention is done.
+__host__ __device__ inline int step_head_bytes(int attn_bytes, int parts, int K) {
+  const int m = merge_lds_bytes(parts, K);
+  return attn_bytes > m ? attn_bytes : m;
+}
+
 template <typename T, int D, int RT, int U, bool IL>
 __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     Shape sh, const T* __restrict__ q, const T* __restrict__ pool, const T* __restrict__ summ,
     const int32_t* __restrict__ ctx, float scale, int step, int max_admit, T* __restrict__ out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l,
-    int32_t* last_sel, int32_t* admit, int32_t* admit_count, int parts, StepWorkspace ws) {
+    int32_t* last_sel, int32_t* admit, int32_t* admit_count, int parts, bool ordered,
+    StepWorkspace ws) {
   extern __shared__ __align__(16) char smem[];
   constexpr bool kMfma = sizeof(T) == 2;
   const int units = sh.B * sh.H;
-  const int unit = blockIdx.x % units;
-  const int part = blockIdx.x / units;
+  int unit = blockIdx.x % units;
+  const int slot = blockIdx.x / units;
+  int sp = -1;                             // scan part, ordered mapping
+  if (!IL && ordered && slot >= 1 && !scan_item<false>(sh, ctx, blockIdx.x - units, unit, sp))
+    return;
   const int b = unit / sh.H, h = unit % sh.H;
   const int tid = threadIdx.x;
-  const int attn_bytes = kMfma ? attn_region(D, RT) : attn_f32_lds_bytes(D);
-  const SelectPtrs p = select_ptrs(smem + attn_bytes, sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk,
+  const int head = step_head_bytes(kMfma ? attn_region(D, RT) : attn_f32_lds_bytes(D), parts, sh.K);
+  const SelectPtrs p = select_ptrs(smem + head, sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk,
                                    sh.K);
   // the unit's top-K list out, then the capped eviction (kk = list length)
   auto finish = [&](int kk) {
@@ -460,15 +671,6 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
                p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
                admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
-  };
-  // a scan part's list to the workspace (chunk c in slot 1 + c of the unit)
-  auto publish = [&](int kk, int c0, int chunk) {
-    const size_t slot = (size_t)unit * parts + 1 + chunk;
-    for (int t = tid; t < sh.K; t += kThreads) {
-      ws.key[slot * sh.K + t] = t < kk ? p.sel_key[t] : 0u;
-      ws.idx[slot * sh.K + t] = t < kk ? c0 + p.sel_idx[t] : -1;
-    }
-    if (tid == 0) ws.n[slot] = kk;
   };
   if constexpr (IL && kMfma) {
     // Launched only when every context fits one scan part (one workgroup per
@@ -487,6 +689,15 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   const int L = ctx[b];
   const int nb = n_blocks(L, sh.NBmax);
   const int active = nb > kScanChunk ? 1 + scan_parts(nb) : 1;
+  // Without the ordered mapping (more than kOrderedMaxBatch requests) a split
+  // unit's last (shortest) scan part takes the last slot: workgroups start in
+  // slot order, so the launch ends on short workgroups instead of full
+  // 1024-block scans started when the first ones drain.
+  int part = slot;
+  if (sp >= 0)
+    part = 1 + sp;
+  else if (active > 1 && slot >= 1)
+    part = slot == parts - 1 ? active - 1 : (slot < active - 1 ? slot : active);
   if (part >= active) return;
   const bool whole = active == 1;          // one workgroup does the whole unit
   const int c0 = whole ? 0 : (part - 1) * kScanChunk;
@@ -504,100 +715,28 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     return topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
                                             p.cand_key, p.ev.red);
   };
-  int kk = 0;
   if (!whole) {
-    if (part == 0) attention();
-    else kk = scan_select();
-  } else if (scan_first(unit)) {
+    __shared__ int last;
+    if (part == 0) {
+      attention();
+    } else {
+      const int kk = scan_select();
+      publish_list(sh, ws, unit, parts, part - 1, c0, kk, p);
+    }
+    if (!arrive_last(ws, unit, active, &last)) return;
+    merge_unit<true, true>(sh, unit, active - 1, step, max_admit, topk_idx, topk_score, l2p, p2l,
+                           last_sel, admit, admit_count, parts, ws, p, smem);
+    return;
+  }
+  int kk;
+  if (scan_first(unit)) {
     kk = scan_select();
     attention();
   } else {
     attention();
     kk = scan_select();
   }
-
-  if (!whole) {
-    if (part == 0) return;                 // attention only
-    publish(kk, c0, part - 1);
-    return;                                // split_select_kernel finishes the unit
-  }
   finish(kk);
-}
-
-// Second kernel of a split step: for every unit whose context exceeds
-// kScanChunk blocks, the scan parts' lists (each sorted by (key desc, block
-// asc), covering ascending block ranges) are concatenated in part order, so
-// equal keys stay in ascending block order and the final top-K equals that of
-// one scan over the whole context; then the capped eviction (EVICT: the fused
-// step; the standalone scan + top-K stops after the list).  (Loading the list
-// slots with the context length in one round trip, from padded lists, and
-// dropping entries below the largest K-th key of the lists measured no gain.)
-template <bool EVICT>
-__global__ __launch_bounds__(kThreads) void split_select_kernel(
-    Shape sh, const int32_t* __restrict__ ctx, int step, int max_admit,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int32_t* l2p, int32_t* p2l,
-    int32_t* last_sel, int32_t* admit, int32_t* admit_count, int parts, StepWorkspace ws) {
-  extern __shared__ __align__(16) char smem[];
-  const int unit = blockIdx.x;
-  const int nb = n_blocks(ctx[unit / sh.H], sh.NBmax);
-  if (nb <= kScanChunk) return;            // finished by the scan kernel
-  const int active = 1 + scan_parts(nb);
-  const int tid = threadIdx.x;
-  const SelectPtrs p = select_ptrs(smem, 0, sh.K);
-  uint32_t* mkey = reinterpret_cast<uint32_t*>(smem + SelectLds(0, sh.K).total);
-  int* midx = reinterpret_cast<int*>(mkey + parts * sh.K);
-  // every part's length at once, then all entries in one pass (loads issued
-  // unconditionally; entries past a list's length are not stored)
-  int* lens = p.ev.red;                       // the eviction's counters are free here
-  const int np = active - 1;                  // scan parts, 1 .. 8
-  if (tid < np) {
-    const int n = ws.n[(size_t)unit * parts + 1 + tid];
-    lens[tid] = n < 0 ? 0 : (n > sh.K ? sh.K : n);
-  }
-  __syncthreads();
-  int total = 0;
-  for (int pp = 0; pp < np; ++pp) total += lens[pp];
-  for (int e = tid; e < np * sh.K; e += kThreads) {
-    const int pp = e / sh.K, r = e % sh.K;
-    const size_t sl = (size_t)unit * parts + 1 + pp;
-    const uint32_t k = ws.key[sl * sh.K + r];
-    const int i = ws.idx[sl * sh.K + r];
-    int off = 0;
-    for (int x = 0; x < pp; ++x) off += lens[x];
-    if (r < lens[pp]) {
-      mkey[off + r] = k;
-      midx[off + r] = i;
-    }
-  }
-  __syncthreads();
-  // at most 8192 / kScanChunk lists of K <= 256 entries
-  // keys per thread sized to the unit's list total (the selection's passes
-  // run over every register slot, filled or not; the result does not depend
-  // on the slot count)
-  constexpr int kMergeKpt = (8192 / kScanChunk) * 256 / kThreads;
-  int kk;
-  if (total <= kThreads)
-    kk = topk_unit<1>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
-  else if (total <= 2 * kThreads)
-    kk = topk_unit<2>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
-  else if (total <= 4 * kThreads)
-    kk = topk_unit<4>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
-  else
-    kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key,
-                              p.ev.red);
-  for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
-  __syncthreads();
-  for (int t = tid; t < sh.K; t += kThreads) {
-    if (t >= kk) p.sel_idx[t] = -1;
-    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
-    topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
-  }
-  if constexpr (EVICT) {
-    __syncthreads();
-    evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
-               p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
-               admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
-  }
 }
 
 // ------------------------------------------------------------------ dense attention
@@ -700,6 +839,13 @@ constexpr size_t kMaxLds = 64 * 1024;   // dynamic LDS per workgroup
 float scale_or_default(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
 
 int rt_of(int G) { return 2 * G <= 16 ? 1 : 2; }
+
+// A tag for one launch's arrival words: odd in bits 16..63, zero below.
+std::atomic<unsigned long long> g_launches{0};
+unsigned long long launch_tag() {
+  const unsigned long long t = g_launches.fetch_add(1, std::memory_order_relaxed) + 1;
+  return ((t << 1) | 1ull) << 16;
+}
 }  // namespace
 
 hipError_t launch_summarize(const Shape& sh, int dtype, const void* records, const int32_t* ctx,
@@ -755,22 +901,18 @@ hipError_t launch_score_topk(const Shape& sh, int dtype, const void* q, int q_ro
   const int parts = step_parts(sh.NBmax);
   if (parts > 1) {
     // split over scan parts, then merge the parts' lists
-    const StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
-    const size_t lds = SelectLds(kScanChunk, sh.K).total;
+    StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
+    ws.tag = launch_tag();
+    const size_t lds = merge_lds_bytes(parts, sh.K) + SelectLds(kScanChunk, sh.K).total;
+    if (lds > kMaxLds) return hipErrorInvalidConfiguration;
     dim3 pgrid(sh.B * sh.H * scan_parts(sh.NBmax));
 #define OASIS_PART(T_, D_)                                                                    \
   hipLaunchKernelGGL((score_part_kernel<T_, D_, 8>), pgrid, dim3(kThreads), lds, st, sh,      \
-                     (const T_*)q, q_row, (const T_*)summ, ctx, topk_idx, topk_score, parts, ws)
+                     (const T_*)q, q_row, (const T_*)summ, ctx, topk_idx, topk_score, parts,   \
+                     sh.B <= kOrderedMaxBatch, ws)
     if (dtype == 1) { if (sh.d == 128) { OASIS_PART(uint16_t, 128); } else { OASIS_PART(uint16_t, 64); } }
     else            { if (sh.d == 128) { OASIS_PART(float, 128); }    else { OASIS_PART(float, 64); } }
 #undef OASIS_PART
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t mlds = SelectLds(0, sh.K).total + (size_t)parts * sh.K * 8;
-    if (mlds > kMaxLds) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(split_select_kernel<false>, dim3(sh.B * sh.H), dim3(kThreads),
-                       mlds, st, sh, ctx, 0, 0, topk_idx, topk_score, nullptr, nullptr, nullptr,
-                       nullptr, nullptr, parts, ws);
     return hipGetLastError();
   }
   dim3 grid(sh.B * sh.H);
@@ -863,12 +1005,14 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
                              int32_t* admit_count, void* workspace, hipStream_t st) {
   const float sc = scale_or_default(scale, sh.d);
   const int parts = step_parts(sh.NBmax);      // list slots per unit (slot 0 unused)
-  const StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
+  StepWorkspace ws = step_workspace(workspace, sh.B * sh.H, parts, sh.K);
+  ws.tag = launch_tag();
+  const bool ordered = sh.B <= kOrderedMaxBatch;
   dim3 grid(sh.B * sh.H * parts);
   const size_t sel = SelectLds(sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk, sh.K).total;
   if (dtype == 1) {
     const int rt = rt_of(sh.G);
-    const size_t lds = attn_region(sh.d, rt) + sel;
+    const size_t lds = step_head_bytes(attn_region(sh.d, rt), parts, sh.K) + sel;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
     const float sl = sc * kLog2e;
     // One scan part per unit: attention and scan interleaved in one pass (at
@@ -880,7 +1024,7 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
   hipLaunchKernelGGL((layer_step_kernel<uint16_t, D_, RT_, U_, IL_>), grid, dim3(kThreads), lds, \
                      st, sh, (const uint16_t*)q, (const uint16_t*)pool, (const uint16_t*)summ,   \
                      ctx, sl, step, max_admit, (uint16_t*)out, topk_idx, topk_score, l2p, p2l,   \
-                     last_sel, admit, admit_count, parts, ws)
+                     last_sel, admit, admit_count, parts, ordered, ws)
     if (parts == 1) {
       if (sh.d == 128) { if (rt == 1) OASIS_STEP(128, 1, 8, true); else OASIS_STEP(128, 2, 8, true); }
       else             { if (rt == 1) OASIS_STEP(64, 1, 8, true);  else OASIS_STEP(64, 2, 8, true); }
@@ -890,24 +1034,15 @@ hipError_t launch_layer_step(const Shape& sh, int dtype, const void* q, const vo
     }
 #undef OASIS_STEP
   } else {
-    const size_t lds = attn_f32_lds_bytes(sh.d) + sel;
+    const size_t lds = step_head_bytes(attn_f32_lds_bytes(sh.d), parts, sh.K) + sel;
     if (lds > kMaxLds) return hipErrorInvalidConfiguration;
 #define OASIS_STEP32(D_)                                                                        \
   hipLaunchKernelGGL((layer_step_kernel<float, D_, 1, 4, false>), grid, dim3(kThreads), lds, st, sh,    \
                      (const float*)q, (const float*)pool, (const float*)summ, ctx, sc, step,     \
                      max_admit, (float*)out, topk_idx, topk_score, l2p, p2l, last_sel, admit,    \
-                     admit_count, parts, ws)
+                     admit_count, parts, ordered, ws)
     if (sh.d == 128) OASIS_STEP32(128); else OASIS_STEP32(64);
 #undef OASIS_STEP32
-  }
-  if (parts > 1) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t lds = SelectLds(0, sh.K).total + (size_t)parts * sh.K * 8;
-    if (lds > kMaxLds) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(split_select_kernel<true>, dim3(sh.B * sh.H), dim3(kThreads), lds, st, sh,
-                       ctx, step, max_admit, topk_idx, topk_score, l2p, p2l, last_sel, admit,
-                       admit_count, parts, ws);
   }
   return hipGetLastError();
 }

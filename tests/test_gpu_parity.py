@@ -152,9 +152,10 @@ def test_topk_with_more_slots_than_blocks_and_large_context():
 @pytest.mark.parametrize("dtype,K,d", [("bf16", 1, 128), ("bf16", 37, 64), ("bf16", 128, 128),
                                        ("bf16", 256, 128), ("f32", 128, 64)])
 def test_score_topk_split_over_scan_parts_exact_on_integer_inputs(dtype, K, d):
-    # contexts past 1024 blocks: one workgroup per 1024-block part, then a
-    # merge launch; contexts on and around the part boundaries, one that fits
-    # a single part (finished by its part workgroup) and an empty request
+    # contexts past 1024 blocks: one workgroup per 1024-block part, the last
+    # of a unit's parts to finish merges the lists; contexts on and around the
+    # part boundaries, one that fits a single part (finished by its part
+    # workgroup) and an empty request
     cfg = small(dtype=dtype, batch=7, k_resident=K, head_dim=d, n_q_heads=8, n_kv_heads=2,
                 planted=0)
     ctx = [16 * 1024, 16 * 1024 + 1, 16 * 2048 + 15, 16 * 5000 - 3, 700, 0, 131072]
@@ -354,8 +355,8 @@ def test_fused_step_equals_separate_calls(case):
                                               ("bf16", 64, 8, 2, 64)])
 def test_fused_step_split_scan_equals_separate_calls(dtype, K, hq, hkv, d):
     # contexts past 1024 blocks split the scan over several workgroups whose
-    # lists a second launch merges; the result must equal one workgroup's
-    # (separate calls)
+    # lists the unit's last workgroup to finish merges; the result must equal
+    # one workgroup's (separate calls)
     # K = 256 at 8192 blocks: the merge sees its largest input, 8 lists of 256;
     # 32 query heads per 2 KV heads: two row tiles; d = 64
     cfg = small(dtype=dtype, batch=4, k_resident=K, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
@@ -376,6 +377,127 @@ def test_fused_step_split_scan_equals_separate_calls(dtype, K, hq, hkv, d):
         for name in ("out", "topk_idx", "topk_score", "l2p", "p2l", "last_sel", "admit",
                      "admit_count"):
             assert torch.equal(getattr(a, name), getattr(b, name)), (step, name)
+
+
+def fill_garbage(ws: torch.Tensor, kind: int) -> None:
+    """Workspace contents a caller might hand over: all ones, random bytes,
+    or arrival words holding large counts."""
+    if kind == 0:
+        ws.fill_(0xFF)
+    elif kind == 1:
+        g = torch.Generator(device="cpu").manual_seed(77)
+        ws.copy_(torch.randint(0, 256, ws.shape, generator=g, dtype=torch.uint8))
+    else:
+        ws.view(torch.int64)[:].fill_(0x0123456789AB0007)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_split_step_needs_no_workspace_initialisation(kind):
+    # a split unit's workgroups count their arrivals in the workspace; stale or
+    # random contents there (another shape's lists, never-written memory)
+    # must not change the result
+    cfg = small(dtype="bf16", batch=4, k_resident=128, n_q_heads=8, n_kv_heads=2, planted=0)
+    ctx = [131072, 40000, 16 * 1024 + 1, 900]
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=31)
+    state = gen.random_state(cfg, ctx, nbmax, 31, fill=0.9, stamp_max=3)
+    a, b = Layer(cfg, ctx, nbmax), Layer(cfg, ctx, nbmax)
+    for L in (a, b):
+        L.summarize(rec)
+        L.set_state(*state)
+        L.pool.copy_(pool_from_records(rec, L.p2l))
+    for step in (4, 5):
+        fill_garbage(a.workspace, kind)
+        a.step(q, step)
+        b.step_unfused(q, step)
+        torch.cuda.synchronize()
+        for name in ("out", "topk_idx", "topk_score", "l2p", "p2l", "last_sel", "admit",
+                     "admit_count"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (kind, step, name)
+    fill_garbage(a.workspace, kind)
+    a.topk_idx.fill_(-7)
+    lib.score_topk(a.shape, q, a.summ, a.ctx_len, a.topk_idx, a.topk_score, workspace=a.workspace)
+    b.topk_idx.fill_(-9)
+    lib.score_topk(b.shape, q, b.summ, b.ctx_len, b.topk_idx, b.topk_score, workspace=b.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.topk_score, b.topk_score)
+
+
+def test_split_shapes_share_one_workspace():
+    # launches of different shapes on one workspace buffer: the arrival words
+    # and list slots of one shape overlap other data of the next
+    big = small(dtype="bf16", batch=6, k_resident=64, n_q_heads=8, n_kv_heads=2, planted=0)
+    ctx_big = [16 * 8192, 16 * 3000 + 5, 16 * 1024 + 1, 16 * 2048, 5, 16 * 6000]
+    ctx_big, nb_big, rec_big, q_big = setup(big, ctx_big, seed=32, integer=True)
+    sml = small(dtype="bf16", batch=3, k_resident=128, n_q_heads=4, n_kv_heads=4, planted=0)
+    ctx_sml = [16 * 1500, 16 * 2100 + 3, 16 * 700]
+    ctx_sml, nb_sml, rec_sml, q_sml = setup(sml, ctx_sml, seed=33, integer=True)
+    Lb, Ls = Layer(big, ctx_big, nb_big), Layer(sml, ctx_sml, nb_sml)
+    shared = Lb.workspace
+    assert Ls.workspace is not None and Ls.workspace.numel() <= shared.numel()
+    Ls.workspace = shared
+    for L, rec, ctx, seed in ((Lb, rec_big, ctx_big, 32), (Ls, rec_sml, ctx_sml, 33)):
+        L.summarize(rec)
+        L.state0 = gen.random_state(L.cfg, ctx, L.nbmax, seed, fill=0.9, stamp_max=3)
+        L.set_state(*L.state0)
+        L.pool.copy_(pool_from_records(rec, L.p2l))
+    m_b = lib.cap_to_max_admit(big.cap, big.k_resident)
+    m_s = lib.cap_to_max_admit(sml.cap, sml.k_resident)
+    refs = {}
+    for L, cfg, rec, q, ctx, m in ((Lb, big, rec_big, q_big, ctx_big, m_b),
+                                   (Ls, sml, rec_sml, q_sml, ctx_sml, m_s)):
+        refs[id(L)] = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, L.state0, 5, m)
+    # big, small, big again (the small shape's words now sit in the big one's lists)
+    for L, q, m in ((Lb, q_big, m_b), (Ls, q_sml, m_s), (Lb, q_big, m_b)):
+        L.set_state(*L.state0)
+        L.step(q, 5, m)
+        torch.cuda.synchronize()
+        ref = refs[id(L)]
+        check_attention(L.out, ref["out"], L.cfg.dtype)
+        np.testing.assert_array_equal(i32(L.topk_idx), ref["idx"])
+        for k in ("l2p", "p2l"):
+            np.testing.assert_array_equal(i32(getattr(L, k)), ref[k])
+        np.testing.assert_array_equal(i32(L.admit), ref["admit"])
+        np.testing.assert_array_equal(i32(L.admit_count), ref["count"])
+
+
+@pytest.mark.parametrize("batch,longest", [(130, 2100), (260, 1100)])
+def test_split_step_workgroup_orders(batch, longest):
+    # long contexts among many requests: up to 256 requests the scan
+    # workgroups follow the length-ordered mapping (here over three 64-request
+    # groups), above it the fixed one; both must give the oracle's result
+    cfg = small(dtype="bf16", batch=batch, k_resident=16, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                planted=0)
+    rng = np.random.default_rng(batch)
+    ctx = rng.integers(0, 16 * 300, batch)
+    longs = rng.choice(batch, 24, replace=False)
+    ctx[longs] = rng.integers(16 * 1000, 16 * longest, 24)
+    ctx[longs[:2]] = [16 * 1024, 16 * 1024 + 1]                  # on a part boundary
+    ctx[longs[2]] = 16 * longest
+    ctx, nbmax, rec, q = setup(cfg, ctx, seed=34, integer=True)
+    say(f"batch {batch}: NBmax {nbmax}, {int(np.sum(ctx > 16 * 1024))} split requests")
+    state = gen.random_state(cfg, ctx, nbmax, 34, fill=0.8, stamp_max=3)
+    layer = Layer(cfg, ctx, nbmax)
+    layer.summarize(rec)
+    layer.set_state(*state)
+    layer.pool.copy_(pool_from_records(rec, layer.p2l))
+    m = lib.cap_to_max_admit(cfg.cap, cfg.k_resident)
+    layer.step(q, 5, m)
+    torch.cuda.synchronize()
+    ref = oracle_step(cfg, rec.cpu(), q.cpu(), ctx, state, 5, m)
+    check_attention(layer.out, ref["out"], cfg.dtype)
+    np.testing.assert_array_equal(i32(layer.topk_idx), ref["idx"])
+    for k in ("l2p", "p2l"):
+        np.testing.assert_array_equal(i32(getattr(layer, k)), ref[k])
+    np.testing.assert_array_equal(i32(layer.last_sel), ref["ls"])
+    np.testing.assert_array_equal(i32(layer.admit), ref["admit"])
+    np.testing.assert_array_equal(i32(layer.admit_count), ref["count"])
+    layer.topk_idx.fill_(-7)
+    lib.score_topk(layer.shape, q, layer.summ, layer.ctx_len, layer.topk_idx, layer.topk_score,
+                   workspace=layer.workspace)
+    torch.cuda.synchronize()
+    idx, val = oracle.topk(ref["scores"], ctx, 16, cfg.k_resident)
+    np.testing.assert_array_equal(i32(layer.topk_idx), idx)
+    np.testing.assert_array_equal(host(layer.topk_score).astype(np.float64), val)
 
 
 def oracle_step(cfg, rec, q, ctx, state, step, m):
