@@ -8,6 +8,8 @@
         --stats DIR3 --copy-kernel elementwise --copy-bytes N \
         --cmd-fetch "..." --cmd-write "..." --cmd-stats "..." --out profiles/X.md
     python -m sparse_kv_block_amd.profiling pipeline BENCH.json --cmd "..." --out profiles/X.md
+    python -m sparse_kv_block_amd.profiling sq NAME=DIR ... --kernel layer_step --cmd "..." \
+        --out profiles/X.md
 
 `counters` scales the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
 what the same counters read for a plain copy kernel of known size, and records
@@ -197,6 +199,55 @@ def pipeline(bench_json: str, cmd: str, out: str):
     return text
 
 
+SQ_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_ANY",
+               "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_VALU_MFMA_BUSY_CYCLES",
+               "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS"]
+
+
+def sq(runs, substr: str, cmd: str, out: str, xcds: int = 8, simds: int = 1024):
+    """Median per dispatch of each SQ/GRBM counter of the kernels matching
+    `substr`, one column per run (NAME=DIR), and two shares of the SIMD
+    cycles: VALU issue (SQ_INSTS_VALU x 4 cycles, one wave64 instruction on a
+    16-lane SIMD) and MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES), each over the
+    kernel's cycles (GRBM_GUI_ACTIVE, summed over the XCDs) x the SIMDs."""
+    cols = []
+    for spec in runs:
+        name, d = spec.split("=", 1)
+        rows = _rows(_find(d, "counter_collection.csv"))
+        per = {}
+        for r in rows:
+            if substr not in r.get("Kernel_Name", ""):
+                continue
+            c = r["Counter_Name"]
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            per.setdefault(c, {})
+            per[c][key] = per[c].get(key, 0.0) + float(r["Counter_Value"])
+        if not per:
+            raise ValueError(f"no rows for kernels matching {substr!r} in {d}")
+        cols.append((name, {c: statistics.median(v.values()) for c, v in per.items()},
+                     len(next(iter(per.values())))))
+    lines = ["# SQ counters of the fused layer step", "",
+             f"Kernel sources: {kernel_source_hash()}.  Median per dispatch of kernels matching "
+             f"`{substr}`; one rocprofv3 pass per workload (command below, NAME = the workload).", "",
+             "| counter | " + " | ".join(n for n, _, _ in cols) + " |",
+             "|---|" + "---|" * len(cols)]
+    for c in SQ_COUNTERS:
+        if all(c in m for _, m, _ in cols):
+            lines.append(f"| {c} | " + " | ".join(f"{m[c]:.4g}" for _, m, _ in cols) + " |")
+    lines.append("| dispatches | " + " | ".join(str(k) for _, _, k in cols) + " |")
+    cyc = [m["GRBM_GUI_ACTIVE"] / xcds * simds for _, m, _ in cols]
+    lines.append("| VALU issue share | " + " | ".join(
+        f"{m['SQ_INSTS_VALU'] * 4 / y:.1%}" for (_, m, _), y in zip(cols, cyc)) + " |")
+    lines.append("| MFMA busy share | " + " | ".join(
+        f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / y:.1%}" for (_, m, _), y in zip(cols, cyc)) + " |")
+    lines += ["", f"Shares: over GRBM_GUI_ACTIVE / {xcds} XCDs x {simds} SIMDs; VALU = "
+              "SQ_INSTS_VALU x 4 cycles.", "", "Command:", "", "    " + cmd, ""]
+    text = "\n".join(lines)
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -229,7 +280,15 @@ def main():
     pp.add_argument("bench_json")
     pp.add_argument("--cmd", required=True)
     pp.add_argument("--out", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("runs", nargs="+")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--cmd", required=True)
+    q.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.what == "sq":
+        print(sq(a.runs, a.kernel, a.cmd, a.out))
+        return
     if a.what == "pipeline":
         print(pipeline(a.bench_json, a.cmd, a.out))
         return
