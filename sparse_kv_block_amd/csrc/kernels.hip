@@ -246,11 +246,13 @@ __host__ __device__ inline int merge_lds_bytes(int parts, int K) {
 // over the whole context; then the list out and (EVICT) the capped eviction.
 // COHERENT: the lists were written in the same launch.
 template <bool EVICT, bool COHERENT>
-__device__ void merge_unit(const Shape& sh, int unit, int np, int step, int max_admit,
-                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_score,
-                           int32_t* l2p, int32_t* p2l, int32_t* last_sel, int32_t* admit,
-                           int32_t* admit_count, int parts, const StepWorkspace& ws,
-                           const SelectPtrs& p, char* merge_lds) {
+__device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, int step,
+                                           int max_admit, int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_score, int32_t* l2p,
+                                           int32_t* p2l, int32_t* last_sel, int32_t* admit,
+                                           int32_t* admit_count, int parts,
+                                           const StepWorkspace& ws, const SelectPtrs& p,
+                                           char* merge_lds) {
   const int tid = threadIdx.x;
   uint32_t* mkey = reinterpret_cast<uint32_t*>(merge_lds);
   int* midx = reinterpret_cast<int*>(mkey + (parts - 1) * sh.K);
@@ -318,8 +320,8 @@ __device__ void merge_unit(const Shape& sh, int unit, int np, int step, int max_
 // Returns false past the last item.  Every wave computes the same result:
 // one ballot per group and 64 requests, twice.
 template <bool SINGLE>
-__device__ bool scan_item(const Shape& sh, const int32_t* __restrict__ ctx, int j, int& unit,
-                          int& sp) {
+__device__ __forceinline__ bool scan_item(const Shape& sh, const int32_t* __restrict__ ctx, int j,
+                                          int& unit, int& sp) {
   constexpr int kFull = 8192 / kScanChunk;       // groups of full parts
   constexpr int kBands = kScanChunk / 128;       // groups of last parts
   const int lane = threadIdx.x & (kWave - 1);
