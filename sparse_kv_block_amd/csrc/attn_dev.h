@@ -65,11 +65,16 @@ struct AttnWave {
   f32x4 acc[TW][NT];
   const uint16_t* unit_pool;
 
-  // unit_base: the unit's first record (slot 0 of its pool, or block 0 of its
-  // records for the dense variant).  q_area: QLDS_BYTES of LDS (QL only).
-  __device__ __forceinline__ void init(const Shape& sh, const uint16_t* __restrict__ q,
-                                       const uint16_t* __restrict__ unit_base, int b, int h,
-                                       void* q_area = nullptr) {
+  // query operand: lane (g, n) holds row 16*(rt+t) + n, channels 32*kk + 8g .. +8.
+  // init_load issues the operand loads (a row past 2G loads row 0 and is
+  // zeroed in init_commit), so that callers can issue their other start-up
+  // loads before the first wait: with each load inside `if (valid)` and the
+  // LDS store after it, the compiler waited a full round trip per operand.
+  u32x4 qraw[TW][KS];
+  bool qvalid[TW];
+
+  __device__ __forceinline__ void init_load(const Shape& sh, const uint16_t* __restrict__ q, int b,
+                                            int h) {
     const int lane = threadIdx.x % kWave;
     w = threadIdx.x / kWave;
     g = lane >> 4;
@@ -77,23 +82,33 @@ struct AttnWave {
     rt = kPairs ? (w & 1) : 0;
     split = kPairs ? (w >> 1) : w;
     const int G = sh.G;
+    // with QL only wave 0 needs the operands (it stores them for all)
+    if (QL && w != 0) return;
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
-      // query operand: lane (g, n) holds row 16*(rt+t) + n, channels 32*kk + 8g .. +8
       const int r = 16 * (rt + t) + n;
-      const bool valid = r < 2 * G;
-      const int row = r < G ? 0 : 1;
-      const int head = h * G + (r < G ? r : r - G);
+      qvalid[t] = r < 2 * G;
+      const int rc = qvalid[t] ? r : 0;
+      const int row = rc < G ? 0 : 1;
+      const int head = h * G + (rc < G ? rc : rc - G);
       const uint16_t* qr = q + ((size_t)(b * 2 + row) * sh.Hq + head) * D;
 #pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        qraw[t][kk] = *reinterpret_cast<const u32x4*>(qr + 32 * kk + 8 * g);
+    }
+  }
+
+  // unit_base: the unit's first record (slot 0 of its pool, or block 0 of its
+  // records for the dense variant).  q_area: QLDS_BYTES of LDS (QL only).
+  __device__ __forceinline__ void init_commit(const uint16_t* __restrict__ unit_base,
+                                              void* q_area = nullptr) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+#pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        bf16x8 v;
-        if (valid) {
-          v = *reinterpret_cast<const bf16x8*>(qr + 32 * kk + 8 * g);
-        } else {
-          u32x4 z = {0u, 0u, 0u, 0u};
-          v = __builtin_bit_cast(bf16x8, z);
-        }
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const bf16x8 v = __builtin_bit_cast(bf16x8, qvalid[t] ? qraw[t][kk] : z);
         if constexpr (QL) {
           if (w == 0) static_cast<bf16x8*>(q_area)[(t * KS + kk) * kWave + lane] = v;
         } else {
@@ -107,6 +122,13 @@ struct AttnWave {
     }
     unit_pool = unit_base;
     qlds = static_cast<const bf16x8*>(q_area);
+  }
+
+  __device__ __forceinline__ void init(const Shape& sh, const uint16_t* __restrict__ q,
+                                       const uint16_t* __restrict__ unit_base, int b, int h,
+                                       void* q_area = nullptr) {
+    init_load(sh, q, b, h);
+    init_commit(unit_base, q_area);
   }
 
   // This wave's slots are split, split + NSPLIT, split + 2*NSPLIT, ...: the
@@ -282,23 +304,36 @@ struct AttnWave {
       }
       __syncthreads();
     }
+    // eight consecutive channels of one row per thread and pass: one 16-byte
+    // store of the normalised bf16 row slice
     const int rows = 2 * G;
-    for (int e = tid; e < rows * D; e += kThreads) {
-      const int r = e / D, c = e % D;
+    constexpr int CV = 8;
+    for (int e = tid; e < rows * (D / CV); e += kThreads) {
+      const int r = e / (D / CV), c0 = (e % (D / CV)) * CV;
       const int rr = r % 16, tile = r / 16;
-      float o;
-      if (kPairs) o = obuf[tile * D * 17 + c * 17 + rr];
-      else o = obuf[(tile * 2) * D * 17 + c * 17 + rr] + obuf[(tile * 2 + 1) * D * 17 + c * 17 + rr];
+      float o[CV];
+#pragma unroll
+      for (int i = 0; i < CV; ++i) {
+        const int c = c0 + i;
+        if (kPairs) o[i] = obuf[tile * D * 17 + c * 17 + rr];
+        else o[i] = obuf[(tile * 2) * D * 17 + c * 17 + rr] + obuf[(tile * 2 + 1) * D * 17 + c * 17 + rr];
+      }
       const float Ls = lstar[r];
       if (part) {
         float* pr = part + (size_t)r * (D + 2);
-        if (c == 0) { pr[0] = mstar[r]; pr[1] = Ls; }
-        pr[2 + c] = o;
+        if (c0 == 0) { pr[0] = mstar[r]; pr[1] = Ls; }
+#pragma unroll
+        for (int i = 0; i < CV; ++i) pr[2 + c0 + i] = o[i];
         continue;
       }
       const int row = r < G ? 0 : 1;
       const int head = h * G + (r < G ? r : r - G);
-      out[((size_t)(b * 2 + row) * sh.Hq + head) * D + c] = f32_to_bf16_bits(Ls > 0.f ? o / Ls : 0.f);
+      u32x4 packed;
+#pragma unroll
+      for (int i = 0; i < CV / 2; ++i)
+        packed[i] = (uint32_t)f32_to_bf16_bits(Ls > 0.f ? o[2 * i] / Ls : 0.f) |
+                    ((uint32_t)f32_to_bf16_bits(Ls > 0.f ? o[2 * i + 1] / Ls : 0.f) << 16);
+      *reinterpret_cast<u32x4*>(out + ((size_t)(b * 2 + row) * sh.Hq + head) * D + c0) = packed;
     }
   }
 };

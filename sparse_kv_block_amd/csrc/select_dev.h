@@ -103,30 +103,35 @@ struct Raw {
 // for channels c0 .. c0+CPL: Nq = sum_i min(q_ic, 0), Pq = sum_i max(q_ic, 0).
 // With min_c <= max_c, max(q min_c, q max_c) = min(q, 0) min_c + max(q, 0) max_c,
 // so the group's summed Quest bound is sum_c (Nq_c min_c + Pq_c max_c).
-template <typename T, int D, int CPL>
+// KB query heads' rows in flight at a time (a load-then-add loop waits a full
+// round trip per head), kept as raw words until summed in head order.  The
+// interleaved step with two row tiles takes all of up to 16 heads (every
+// supported group) in one round trip; the other paths four at a time (the
+// raw words of 16 heads would cost the split step a wave per SIMD, and the
+// one-tile step measured slower with 8 or 16).
+template <typename T, int D, int CPL, int KB = 4>
 __device__ __forceinline__ void group_query_sums(const Shape& sh, const T* __restrict__ q,
                                                  int q_row, int b, int h, int c0, float* Nq,
                                                  float* Pq) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i) { Nq[i] = 0.f; Pq[i] = 0.f; }
-  // four query heads' loads in flight at a time (a load-then-add loop waits a
-  // full round trip per head), summed in head order
-  constexpr int kB = 4;
   const T* q0 = q + ((size_t)(b * 2 + q_row) * sh.Hq + h * sh.G) * D + c0;
-  for (int i0 = 0; i0 < sh.G; i0 += kB) {
-    float v[kB][CPL];
+  for (int i0 = 0; i0 < sh.G; i0 += KB) {
+    Raw<T, CPL> r[KB];
 #pragma unroll
-    for (int k = 0; k < kB; ++k) {
+    for (int k = 0; k < KB; ++k) {
       const int i = i0 + k < sh.G ? i0 + k : sh.G - 1;    // clamped, ignored past G
-      Elem<T>::template load<CPL>(q0 + (size_t)i * D, v[k]);
+      r[k].load(q0 + (size_t)i * D);
     }
 #pragma unroll
-    for (int k = 0; k < kB; ++k) {
+    for (int k = 0; k < KB; ++k) {
       const bool in = i0 + k < sh.G;    // a select, not a branch: the loads stay together
+      float v[CPL];
+      r[k].unpack(v);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        Nq[c] = in ? Nq[c] + fminf(v[k][c], 0.f) : Nq[c];
-        Pq[c] = in ? Pq[c] + fmaxf(v[k][c], 0.f) : Pq[c];
+        Nq[c] = in ? Nq[c] + fminf(v[c], 0.f) : Nq[c];
+        Pq[c] = in ? Pq[c] + fmaxf(v[c], 0.f) : Pq[c];
       }
     }
   }

@@ -34,20 +34,38 @@ __device__ __forceinline__ int attn_scan_unit_bf16(const Shape& sh, const uint16
   constexpr int RW = CPL / 2;          // 32-bit words of one summary row slice
   AW a;
   const int unit = b * sh.H + h;
-  // with QL the query operands go to the start of the merge area, which the
-  // merge first writes after its own first barrier
-  a.init(sh, q, pool + (size_t)unit * sh.K * AW::REC, b, h, lds);
-  // the slot map, the query operands and the query sums are loaded together
-  // before the first use of any of them
+  // the query operands, the slot map, the context length and the query rows
+  // of the group sums are all loaded before the first use of any of them
+  a.init_load(sh, q, b, h);
   const int ns = a.n_slots(sh);
   const int j_raw = a.slot_block_raw(sh, p2l, unit, 0, ns);
   const int w = a.w, quad = a.g, n = a.n;
   const int c0 = n * CPL;
-  float Nq[CPL], Pq[CPL];
-  group_query_sums<uint16_t, D, CPL>(sh, q, 1, b, h, c0, Nq, Pq);
   const int L = *ctx_b;
+  float Nq[CPL], Pq[CPL];
+  // with QL the query operands go to the start of the merge area, which the
+  // merge first writes after its own first barrier; the group sums, the same
+  // in every wave, are formed by wave 0 alone and passed on after them
+  float* sums_lds = lds + AW::QLDS_BYTES / 4;      // [16 lanes][2][CPL]
+  if (!QL || w == 0)
+    group_query_sums<uint16_t, D, CPL, (RT == 2 ? 16 : 4)>(sh, q, 1, b, h, c0, Nq, Pq);
+  a.init_commit(pool + (size_t)unit * sh.K * AW::REC, lds);
+  if constexpr (QL) {
+    if (w == 0 && quad == 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        sums_lds[n * 2 * CPL + c] = Nq[c];
+        sums_lds[n * 2 * CPL + CPL + c] = Pq[c];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      Nq[c] = sums_lds[n * 2 * CPL + c];
+      Pq[c] = sums_lds[n * 2 * CPL + CPL + c];
+    }
+  }
   const int nb = n_blocks(L, sh.NBmax);
-  if constexpr (QL) __syncthreads();
   // record groups: group t of wave w holds records 4*kWaves*t + 4*w + quad
   constexpr int GS = 4 * kWaves;
   const int Gw = nb > 4 * w ? (nb - 4 * w + GS - 1) / GS : 0;
