@@ -30,7 +30,7 @@ oasis_status hip_status(hipError_t e, const char* what) {
   return fail(OASIS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kMaxBlocks = 8192;
+using oasis::kMaxBlocks;
 constexpr int kMaxK = 256;
 constexpr int kMaxGroup = 16;
 // Units per call: keeps every per-launch count the kernels form in 32-bit

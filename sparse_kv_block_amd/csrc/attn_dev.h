@@ -26,10 +26,15 @@
 
 namespace oasis {
 
-// LDS bytes the bf16 attention merge needs (two [D][17] partial-output
-// buffers, per-wave row max and sum, per-row denominators).
+// Row stride (floats) of the merge's partial-output buffers: rows of D
+// channels padded by 4, so that the 16 rows' 16-byte accesses at one channel
+// fall on distinct banks.
+__host__ __device__ constexpr int attn_row_stride(int D) { return D + 4; }
+
+// LDS bytes the bf16 attention merge needs (two [16][D + 4] partial-output
+// buffers per row tile, per-wave row max and sum, per-row denominators).
 __host__ __device__ constexpr int attn_lds_bytes(int D, int RT) {
-  return (RT * 2 * D * 17 + kWaves * 16 * RT * 2 + 2 * 16 * RT) * 4;
+  return (RT * 2 * 16 * attn_row_stride(D) + kWaves * 16 * RT * 2 + 2 * 16 * RT) * 4;
 }
 
 // RT = 16-row tiles of the stacked rows (1: up to 16 rows, 2: up to 32).
@@ -241,14 +246,17 @@ struct AttnWave {
   // Merges the waves that share a row tile through LDS and writes the rows:
   // normalised bf16 rows to `out`, or, when `part` is given, the unnormalised
   // partial (running max, sum, output row) of each row to part[r][0 .. D+2).
-  // LDS: [2*TW][D][17] partial outputs, [kWaves][16*TW] max and sum, [16*RT] x 2.
+  // LDS: [2*TW][16][D + 4] partial outputs (row-major: a lane's four
+  // accumulator channels are one 16-byte access), [kWaves][16*TW] max and
+  // sum, [16*RT] x 2.
   __device__ __forceinline__ void merge_store(const Shape& sh, int b, int h,
                                               uint16_t* __restrict__ out, float* lds,
                                               float* __restrict__ part = nullptr) const {
     const int tid = threadIdx.x;
     const int G = sh.G;
-    float* obuf = lds;                                   // [TW][2][D][17]
-    float* mbuf = lds + TW * 2 * D * 17;                 // [kWaves][16*TW]
+    constexpr int S = attn_row_stride(D);
+    float* obuf = lds;                                   // [TW][2][16][S]
+    float* mbuf = lds + TW * 2 * 16 * S;                 // [kWaves][16*TW]
     float* lbuf = mbuf + kWaves * 16 * TW;               // [kWaves][16*TW]
     float* lstar = lbuf + kWaves * 16 * TW;              // [16*RT]
     float* mstar = lstar + 16 * RT;                      // [16*RT]
@@ -290,16 +298,13 @@ struct AttnWave {
       if ((w >> 1) == phase) {
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
-          float* ob = obuf + (t * 2 + (w & 1)) * D * 17;
+          float* ob = obuf + (t * 2 + (w & 1)) * 16 * S + n * S + 4 * g;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int c = 16 * nt + 4 * g + i;
-              float* p = ob + c * 17 + n;
-              const float v = acc[t][nt][i] * fw[t];
-              if (phase == 0) *p = v; else *p += v;
-            }
+          for (int nt = 0; nt < NT; ++nt) {
+            f32x4* p = reinterpret_cast<f32x4*>(ob + 16 * nt);
+            const f32x4 v = acc[t][nt] * fw[t];
+            if (phase == 0) *p = v; else *p += v;
+          }
         }
       }
       __syncthreads();
@@ -312,11 +317,15 @@ struct AttnWave {
       const int r = e / (D / CV), c0 = (e % (D / CV)) * CV;
       const int rr = r % 16, tile = r / 16;
       float o[CV];
+      {
+        const float* s0 = obuf + (kPairs ? tile : tile * 2) * 16 * S + rr * S + c0;
 #pragma unroll
-      for (int i = 0; i < CV; ++i) {
-        const int c = c0 + i;
-        if (kPairs) o[i] = obuf[tile * D * 17 + c * 17 + rr];
-        else o[i] = obuf[(tile * 2) * D * 17 + c * 17 + rr] + obuf[(tile * 2 + 1) * D * 17 + c * 17 + rr];
+        for (int i = 0; i < CV; i += 4) {
+          f32x4 v = *reinterpret_cast<const f32x4*>(s0 + i);
+          if (!kPairs) v += *reinterpret_cast<const f32x4*>(s0 + 16 * S + i);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[i + k] = v[k];
+        }
       }
       const float Ls = lstar[r];
       if (part) {

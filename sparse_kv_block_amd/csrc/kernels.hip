@@ -4,9 +4,9 @@
 // the units are independent (their blocks, summaries, maps and slots are
 // disjoint).  Only a long context's split over several workgroups hands data
 // from one workgroup to another (the scan parts' lists, merged by the last of
-// the unit's workgroups to finish).  At batch 128 x 8 KV heads that is 1024 workgroups; the
-// fused step's register use (about 220 VGPRs, two waves per SIMD) places two
-// per CU, so they run in two even rounds over the 256 CUs.
+// the unit's workgroups to finish).  At batch 128 x 8 KV heads that is 1024
+// workgroups; the fused step's register use (about 210 VGPRs, two waves per
+// SIMD) places two per CU, so they run in two even rounds over the 256 CUs.
 #include <atomic>
 #include <mutex>
 
@@ -126,8 +126,8 @@ __device__ __forceinline__ SelectPtrs select_ptrs(char* smem, int NBmax, int K) 
   p.ev.p2l_s = reinterpret_cast<int*>(smem + lay.p2l_s);
   p.ev.ls_s = reinterpret_cast<int*>(smem + lay.ls_s);
   p.ev.miss = reinterpret_cast<int*>(smem + lay.miss);
-  p.ev.victim = reinterpret_cast<int*>(smem + lay.victim);
   p.ev.vkey = reinterpret_cast<uint64_t*>(smem + lay.vkey);
+  p.ev.bits = reinterpret_cast<uint32_t*>(smem + lay.bits);
   p.ev.red = reinterpret_cast<int*>(smem + lay.red);
   return p;
 }
@@ -259,11 +259,16 @@ __device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, in
   // every part's length, then all entries in one pass (entries past a list's
   // length are not stored).  (Issuing the entry loads with the lengths, in one
   // round trip, measured slower: the registers they hold.)
+  // (EVICT: the slot map and stamps are staged with them)
   int* lens = p.ev.red;                       // the eviction's counters are free here
+  EvictStage ev{};
+  if constexpr (EVICT)
+    ev = evict_load(sh.K, p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K);
   if (tid < np) {
     const int n = ws_load<COHERENT>(&ws.n[(size_t)unit * parts + 1 + tid]);
     lens[tid] = n < 0 ? 0 : (n > sh.K ? sh.K : n);
   }
+  if constexpr (EVICT) evict_commit(sh.K, sh.NBmax, ev, p.ev);
   __syncthreads();
   int total = 0;
   for (int pp = 0; pp < np; ++pp) total += lens[pp];
@@ -280,10 +285,10 @@ __device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, in
     }
   }
   __syncthreads();
-  // at most 8192 / kScanChunk lists of K <= 256 entries; keys per thread
+  // at most kMaxBlocks / kScanChunk lists of K <= 256 entries; keys per thread
   // sized to the unit's list total (the selection's passes run over every
   // register slot, filled or not; the result does not depend on the count)
-  constexpr int kMergeKpt = (8192 / kScanChunk) * 256 / kThreads;
+  constexpr int kMergeKpt = (kMaxBlocks / kScanChunk) * 256 / kThreads;
   int kk;
   if (total <= kThreads)
     kk = topk_unit<1>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
@@ -294,15 +299,15 @@ __device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, in
   else
     kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key,
                               p.ev.red);
-  for (int t = tid; t < kk; t += kThreads) p.sel_idx[t] = midx[p.sel_idx[t]];
-  __syncthreads();
+  // (K <= kThreads: thread t < K owns list entry t from here on, and the
+  // selection ends with a barrier)
   for (int t = tid; t < sh.K; t += kThreads) {
-    if (t >= kk) p.sel_idx[t] = -1;
-    topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
+    const int i = t < kk ? midx[p.sel_idx[t]] : -1;
+    p.sel_idx[t] = i;
+    topk_idx[(size_t)unit * sh.K + t] = i;
     topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
   }
   if constexpr (EVICT) {
-    __syncthreads();
     evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
                p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
                admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
@@ -322,7 +327,7 @@ __device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, in
 template <bool SINGLE>
 __device__ __forceinline__ bool scan_item(const Shape& sh, const int32_t* __restrict__ ctx, int j,
                                           int& unit, int& sp) {
-  constexpr int kFull = 8192 / kScanChunk;       // groups of full parts
+  constexpr int kFull = kMaxBlocks / kScanChunk;       // groups of full parts
   constexpr int kBands = kScanChunk / 128;       // groups of last parts
   const int lane = threadIdx.x & (kWave - 1);
   int full = 0, band = -1, np = 0;
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void agreement_kernel(Shape sh, const int
                                                              const int32_t* __restrict__ l2p,
                                                              int exact_n,
                                                              int32_t* __restrict__ counts) {
-  __shared__ uint32_t bits[8192 / 32];
+  __shared__ uint32_t bits[kMaxBlocks / 32];
   const int unit = blockIdx.x;
   const int words = (sh.NBmax + 31) / 32;
   for (int i = threadIdx.x; i < words; i += kThreads) bits[i] = 0u;
@@ -488,6 +493,9 @@ __global__ __launch_bounds__(kThreads) void evict_kernel(Shape sh, const int32_t
   extern __shared__ __align__(16) char smem[];
   const int unit = blockIdx.x;
   const SelectPtrs p = select_ptrs(smem, 0, sh.K);
+  evict_commit(sh.K, sh.NBmax,
+               evict_load(sh.K, p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K), p.ev);
+  __syncthreads();
   evict_unit(topk_idx + (size_t)unit * sh.K, sh.K, sh.NBmax, step, max_admit,
              l2p + (size_t)unit * sh.NBmax, p2l + (size_t)unit * sh.K,
              last_sel + (size_t)unit * sh.K, admit + (size_t)unit * sh.K * 3, admit_count + unit,
@@ -662,14 +670,14 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   const SelectPtrs p = select_ptrs(smem + head, sh.NBmax < kScanChunk ? sh.NBmax : kScanChunk,
                                    sh.K);
   // the unit's top-K list out, then the capped eviction (kk = list length)
+  // (K <= kThreads: thread t < K owns list entry t here and in the eviction,
+  // and the selection ends with a barrier)
   auto finish = [&](int kk) {
-    __syncthreads();
     for (int t = tid; t < sh.K; t += kThreads) {
       if (t >= kk) p.sel_idx[t] = -1;
       topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
       topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
     }
-    __syncthreads();
     evict_unit(p.sel_idx, sh.K, sh.NBmax, step, max_admit, l2p + (size_t)unit * sh.NBmax,
                p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K,
                admit + (size_t)unit * sh.K * 3, admit_count + unit, p.ev);
@@ -680,9 +688,12 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     // together, two summary groups per block step (with 32 rows the query
     // operands sit in LDS so that both groups fit 2 waves per SIMD).  The
     // context length is read inside, after the query and slot-map loads.
+    // the eviction's slot map and stamps travel with the query loads
+    const EvictStage ev =
+        evict_load(sh.K, p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K);
     const int nb = attn_scan_unit_bf16<D, RT, 2, 8, RT, (RT == 2)>(
         sh, q, pool, p2l, summ + (size_t)unit * sh.NBmax * 2 * D, ctx + b, b, h, scale, out,
-        reinterpret_cast<float*>(smem), p.keys);
+        reinterpret_cast<float*>(smem), p.keys, [&]() { evict_commit(sh.K, sh.NBmax, ev, p.ev); });
     __syncthreads();
     finish(topk_unit<kScanChunk / kThreads>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
                                             p.cand_key, p.ev.red));
@@ -730,6 +741,8 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
                            last_sel, admit, admit_count, parts, ws, p, smem);
     return;
   }
+  evict_commit(sh.K, sh.NBmax,
+               evict_load(sh.K, p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K), p.ev);
   int kk;
   if (scan_first(unit)) {
     kk = scan_select();

@@ -15,6 +15,9 @@ struct Shape {
   int B, Hq, H, G, d, NBmax, K;
 };
 
+// Most blocks per unit (NBmax) the kernels accept.
+constexpr int kMaxBlocks = 8192;
+
 // Bytes of the fused step's split-scan workspace for a shape (0 when every
 // context fits one scan part).
 size_t layer_step_workspace_bytes(const Shape& sh);

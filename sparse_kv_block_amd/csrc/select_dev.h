@@ -22,7 +22,8 @@
 // admitted block is paired with a least-recently-selected resident block):
 // hits are stamped, misses compacted in top-K order with ballots, victims
 // (empty slots first, then stale slots by (stamp, block)) ranked by a 64-bit
-// key, and the maps updated.
+// key, and the maps updated.  Residency is read from the slot map alone (LDS
+// bitmaps of the slots' blocks and of the top-K's), so no l2p entry is read.
 #pragma once
 
 #include "common.h"
@@ -408,16 +409,45 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
 
 // ---------------------------------------------------------------- capped eviction
 struct EvictScratch {
-  int* p2l_s;      // [K]
-  int* ls_s;       // [K]
+  int* p2l_s;      // [K]  the unit's slot map, staged
+  int* ls_s;       // [K]  its last-selected stamps, staged
   int* miss;       // [K]
-  int* victim;     // [K]
-  uint64_t* vkey;  // [K]
+  uint64_t* vkey;  // [K + 2]
+  uint32_t* bits;  // [2][kMaxBlocks / 32]: blocks held by a slot, blocks of T
   int* red;        // [kRedInts]
 };
 
+__host__ __device__ inline int bitmap_words(int NBmax) { return (NBmax + 31) >> 5; }
+
+// Staging of the eviction's inputs: thread t < K loads slot t's block and
+// stamp (evict_load, unconditional clamped loads), then writes them to LDS and
+// clears the bitmaps (evict_commit).  At least one barrier must separate the
+// commit from evict_unit.
+struct EvictStage {
+  int e, st;
+};
+__device__ __forceinline__ EvictStage evict_load(int K, const int32_t* __restrict__ p2l,
+                                                 const int32_t* __restrict__ ls) {
+  const int t = threadIdx.x < K ? threadIdx.x : K - 1;
+  return EvictStage{p2l[t], ls[t]};
+}
+__device__ __forceinline__ void evict_commit(int K, int NBmax, EvictStage v,
+                                             const EvictScratch& x) {
+  const int tid = threadIdx.x;
+  if (tid < K) {
+    x.p2l_s[tid] = v.e;
+    x.ls_s[tid] = v.st;
+  }
+  for (int i = tid; i < 2 * bitmap_words(NBmax); i += kThreads) x.bits[i] = 0u;
+}
+
 // T: the unit's top-K list in LDS or global memory ([K], -1 = unused entry).
-// Pointers l2p/p2l/ls/admit are the unit's slices.
+// Pointers l2p/p2l/ls/admit are the unit's slices; p2l and ls as staged by
+// evict_commit.  l2p and p2l are mutual inverses, so block j is resident
+// exactly when some slot's p2l entry is j: one bit per block held by a slot,
+// one per block of T, and each side tests the other's bits.  Thread t < K
+// then acts for slot t: its stamp, its victim key, and, when it is evicted,
+// its map updates and admission record.
 __device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int step,
                                            int max_admit, int32_t* __restrict__ l2p,
                                            int32_t* __restrict__ p2l, int32_t* __restrict__ ls,
@@ -426,109 +456,102 @@ __device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int s
                                            const EvictScratch& x) {
   const int tid = threadIdx.x;
   const int w = tid / kWave;
-  // the slot lookups of T and the unit's slot map go out in one round trip
+  uint32_t* held_bits = x.bits;
+  uint32_t* sel_bits = x.bits + bitmap_words(NBmax);
+  // 1. membership bits
   const int j = tid < K ? T[tid] : -1;
   const bool valid = j >= 0 && j < NBmax;
-  const int s = valid ? l2p[j] : -1;
-  if (tid < K) {
-    x.p2l_s[tid] = p2l[tid];
-    x.ls_s[tid] = ls[tid];
-  }
+  const int e = tid < K ? x.p2l_s[tid] : -1;
+  int st = tid < K ? x.ls_s[tid] : 0;
+  const bool held = e >= 0 && e < NBmax;
+  if (valid) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+  if (held) atomicOr(&held_bits[e >> 5], 1u << (e & 31));
   __syncthreads();
-  // 1. stamp resident members of T; flag the missing ones
-  const bool hit = valid && s >= 0 && s < K;
-  const bool miss = valid && !hit;
-  if (hit) x.ls_s[s] = step;
-  const uint64_t mm = ballot(miss);
-  if (lane_id() == 0) x.red[w] = __popcll(mm);
-  __syncthreads();
-  int off = 0, nM = 0;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) {
-    off += v < w ? x.red[v] : 0;
-    nM += x.red[v];
-  }
-  if (miss) x.miss[off + lanes_below(mm)] = j;
-  // 2. victim keys: empty slots by slot, then stale slots by (stamp, block)
+  // 2. misses of T; stamps of the slots whose block is in T; victim keys:
+  //    empty slots by slot, then stale slots by (stamp, block)
+  const bool miss = valid && !((held_bits[j >> 5] >> (j & 31)) & 1u);
+  if (held && ((sel_bits[e >> 5] >> (e & 31)) & 1u)) st = step;
   uint64_t key = ~0ull;
   if (tid < K) {
-    const int e = x.p2l_s[tid];
-    const int st = x.ls_s[tid];
     if (e < 0)
       key = (uint64_t)tid;
     else if (st < step)
       key = (1ull << 63) | ((uint64_t)((uint32_t)st ^ 0x80000000u) << 31) | (uint64_t)(uint32_t)e;
     x.vkey[tid] = key;
   }
-  const bool elig = key != ~0ull;
-  const uint64_t me = ballot(elig);
-  if (lane_id() == 0) x.red[kWaves + w] = __popcll(me);
+  if (tid < ((K + 1) & ~1) - K) x.vkey[K + tid] = ~0ull;   // pad to an even count
+  const uint64_t mm = ballot(miss);
+  const uint64_t me = ballot(key != ~0ull);
+  if (lane_id() == 0) {
+    x.red[w] = __popcll(mm);
+    x.red[kWaves + w] = __popcll(me);
+  }
   __syncthreads();
-  int nV = 0;
+  int off = 0, nM = 0, nV = 0;
 #pragma unroll
-  for (int v = 0; v < kWaves; ++v) nV += x.red[kWaves + v];
+  for (int v = 0; v < kWaves; ++v) {
+    off += v < w ? x.red[v] : 0;
+    nM += x.red[v];
+    nV += x.red[kWaves + v];
+  }
   int a = max_admit < nM ? max_admit : nM;
   a = a < nV ? a : nV;
-  a = a < 0 ? 0 : a;
-  if (tid < ((K + 1) & ~1) - K) x.vkey[K + tid] = ~0ull;   // pad to an even count
-  __syncthreads();
-  // rank every eligible key among all K: P threads per candidate, each over
-  // 1/P of the list (every wave busy), partial counts summed through LDS
-  {
-    const int P = K <= kThreads / 4 ? 4 : (K <= kThreads / 2 ? 2 : 1);
-    const int span = kThreads / P;
-    const int c = tid % span, part = tid / span;
+  a = a < 0 ? 0 : a;                       // the same in every thread
+  int rank = a;                            // slot tid's victim rank; >= a: kept
+  if (a > 0) {
+    if (miss) x.miss[off + lanes_below(mm)] = j;
+    // 3. rank every eligible key among all K: P threads per key, each over
+    //    1/P of the list (every wave busy), partial counts summed through LDS
+    const int lp = K <= kThreads / 4 ? 2 : (K <= kThreads / 2 ? 1 : 0);   // log2 of P
+    const int P = 1 << lp;
+    const int span = kThreads >> lp;
+    const int c = tid & (span - 1), part = tid >> (__builtin_ctz(kThreads) - lp);
     const int K2 = (K + 1) >> 1;
-    const int p0 = part * K2 / P, p1 = (part + 1) * K2 / P;
-    int rank = 0;
-    uint64_t ck = ~0ull;
+    const int p0 = (part * K2) >> lp, p1 = ((part + 1) * K2) >> lp;
+    int r = 0;
+    const uint64_t ck = c < K ? x.vkey[c] : ~0ull;
     if (c < K) {
-      ck = x.vkey[c];
 #pragma unroll 8
       for (int p = p0; p < p1; ++p) {
         const u32x4 v = reinterpret_cast<const u32x4*>(x.vkey)[p];
         const uint64_t a0 = ((uint64_t)v[1] << 32) | v[0];
         const uint64_t a1 = ((uint64_t)v[3] << 32) | v[2];
-        rank += (a0 < ck) + (a1 < ck);
+        r += (a0 < ck) + (a1 < ck);
       }
     }
     int* prt = x.red + kRedHist;                       // the radix histograms are free here
-    if (part > 0 && c < K) prt[(part - 1) * span + c] = rank;
-    __syncthreads();
+    if (part > 0 && c < K) prt[(part - 1) * span + c] = r;
+    __syncthreads();                                   // also orders the miss list
     if (part == 0 && c < K && ck != ~0ull) {
-      for (int q = 1; q < P; ++q) rank += prt[(q - 1) * span + c];
-      if (rank < a) x.victim[rank] = c;
+      for (int q = 1; q < P; ++q) r += prt[(q - 1) * span + c];
+      rank = r;
     }
   }
-  __syncthreads();
-  // 3. apply
-  if (tid < a) {
-    const int sv = x.victim[tid];
-    const int old = x.p2l_s[sv];
-    const int aj = x.miss[tid];
-    if (old >= 0 && old < NBmax) l2p[old] = -1;
-    l2p[aj] = sv;
-    x.p2l_s[sv] = aj;
-    x.ls_s[sv] = step;
-    admit[3 * tid + 0] = aj;
-    admit[3 * tid + 1] = sv;
-    admit[3 * tid + 2] = old;
-  } else if (tid < K) {
-    admit[3 * tid + 0] = -1;
-    admit[3 * tid + 1] = -1;
-    admit[3 * tid + 2] = -1;
-  }
-  __syncthreads();
+  // 4. apply: slot tid (tid < K, part 0) takes miss[rank] when rank < a
   if (tid < K) {
-    p2l[tid] = x.p2l_s[tid];
-    ls[tid] = x.ls_s[tid];
+    if (rank < a) {
+      const int aj = x.miss[rank];
+      if (held) l2p[e] = -1;
+      l2p[aj] = tid;
+      p2l[tid] = aj;
+      st = step;
+      admit[3 * rank + 0] = aj;
+      admit[3 * rank + 1] = tid;
+      admit[3 * rank + 2] = e;
+    }
+    ls[tid] = st;
+    if (tid >= a) {
+      admit[3 * tid + 0] = -1;
+      admit[3 * tid + 1] = -1;
+      admit[3 * tid + 2] = -1;
+    }
   }
   if (tid == 0) *admit_count = a;
 }
 
 // LDS layout of the select phase (scan keys + top-K + eviction), in bytes.
 struct SelectLds {
-  int keys, cand_idx, cand_key, sel_idx, sel_key, p2l_s, ls_s, miss, victim, vkey, red, total;
+  int keys, cand_idx, cand_key, sel_idx, sel_key, p2l_s, ls_s, miss, vkey, bits, red, total;
   __host__ __device__ SelectLds(int NBmax, int K) {
     int o = 0;
     auto take = [&](int bytes) { int r = o; o += (bytes + 15) & ~15; return r; };
@@ -540,8 +563,8 @@ struct SelectLds {
     p2l_s = take(K * 4);
     ls_s = take(K * 4);
     miss = take(K * 4);
-    victim = take(K * 4);
     vkey = take((K + 2) * 8);
+    bits = take(2 * (kMaxBlocks / 32) * 4);
     red = take(kRedInts * 4);
     total = o;
   }

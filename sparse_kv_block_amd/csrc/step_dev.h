@@ -20,15 +20,18 @@ namespace oasis {
 // with two).  Reads the request's context length from ctx_b (after issuing
 // the query and slot-map loads, so that the round trips overlap), writes
 // keys[j] for j < nb, returns nb, and ends with the attention merge (so the
-// keys are complete in LDS for the whole workgroup afterwards).
-template <int D, int RT, int SG, int UL, int TW = RT, bool QL = false>
+// keys are complete in LDS for the whole workgroup afterwards).  `staged`
+// runs once the query operands are committed (loads the caller issued before
+// the call have completed by then).
+template <int D, int RT, int SG, int UL, int TW = RT, bool QL = false, typename Staged>
 __device__ __forceinline__ int attn_scan_unit_bf16(const Shape& sh, const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ pool,
                                                    const int32_t* __restrict__ p2l,
                                                    const uint16_t* __restrict__ summ_unit,
                                                    const int32_t* __restrict__ ctx_b, int b, int h,
                                                    float scale_log2, uint16_t* __restrict__ out,
-                                                   float* lds, uint32_t* keys) {
+                                                   float* lds, uint32_t* keys,
+                                                   Staged&& staged) {
   using AW = AttnWave<D, RT, TW, QL>;
   constexpr int CPL = D / 16;
   constexpr int RW = CPL / 2;          // 32-bit words of one summary row slice
@@ -50,6 +53,7 @@ __device__ __forceinline__ int attn_scan_unit_bf16(const Shape& sh, const uint16
   if (!QL || w == 0)
     group_query_sums<uint16_t, D, CPL, (RT == 2 ? 16 : 4)>(sh, q, 1, b, h, c0, Nq, Pq);
   a.init_commit(pool + (size_t)unit * sh.K * AW::REC, lds);
+  staged();
   if constexpr (QL) {
     if (w == 0 && quad == 0) {
 #pragma unroll
