@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(Shape sh, const floa
 struct SelectPtrs {
   uint32_t* keys;
   int* cand_idx;
-  uint32_t* cand_key;
+  uint64_t* cand64;
   int* sel_idx;
   uint32_t* sel_key;
   EvictScratch ev;
@@ -120,7 +120,7 @@ __device__ __forceinline__ SelectPtrs select_ptrs(char* smem, int NBmax, int K) 
   SelectPtrs p;
   p.keys = reinterpret_cast<uint32_t*>(smem + lay.keys);
   p.cand_idx = reinterpret_cast<int*>(smem + lay.cand_idx);
-  p.cand_key = reinterpret_cast<uint32_t*>(smem + lay.cand_key);
+  p.cand64 = reinterpret_cast<uint64_t*>(smem + lay.cand64);
   p.sel_idx = reinterpret_cast<int*>(smem + lay.sel_idx);
   p.sel_key = reinterpret_cast<uint32_t*>(smem + lay.sel_key);
   p.ev.p2l_s = reinterpret_cast<int*>(smem + lay.p2l_s);
@@ -140,7 +140,7 @@ __device__ __forceinline__ void select_from_keys(const Shape& sh, int unit, int 
                                                  int32_t* topk_idx, float* topk_score,
                                                  const SelectPtrs& p) {
   const int kk = topk_unit<KPT>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                p.cand_key, p.ev.red);
+                                p.cand64, p.ev.red);
   for (int t = threadIdx.x; t < sh.K; t += kThreads) {
     if (t >= kk) p.sel_idx[t] = -1;
     topk_idx[(size_t)unit * sh.K + t] = t < kk ? p.sel_idx[t] : -1;
@@ -291,13 +291,13 @@ __device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, in
   constexpr int kMergeKpt = (kMaxBlocks / kScanChunk) * 256 / kThreads;
   int kk;
   if (total <= kThreads)
-    kk = topk_unit<1>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+    kk = topk_unit<1>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64, p.ev.red);
   else if (total <= 2 * kThreads)
-    kk = topk_unit<2>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+    kk = topk_unit<2>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64, p.ev.red);
   else if (total <= 4 * kThreads)
-    kk = topk_unit<4>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key, p.ev.red);
+    kk = topk_unit<4>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64, p.ev.red);
   else
-    kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand_key,
+    kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64,
                               p.ev.red);
   // (K <= kThreads: thread t < K owns list entry t from here on, and the
   // selection ends with a barrier)
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T*
     return;
   }
   const int kk = topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key,
-                                                   p.cand_idx, p.cand_key, p.ev.red);
+                                                   p.cand_idx, p.cand64, p.ev.red);
   publish_list(sh, ws, unit, parts, part, c0, kk, p);
   if (!arrive_last(ws, unit, np, &last)) return;
   merge_unit<false, true>(sh, unit, np, 0, 0, topk_idx, topk_score, nullptr, nullptr, nullptr,
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
         reinterpret_cast<float*>(smem), p.keys, [&]() { evict_commit(sh.K, sh.NBmax, ev, p.ev); });
     __syncthreads();
     finish(topk_unit<kScanChunk / kThreads>(p.keys, nb, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                            p.cand_key, p.ev.red));
+                                            p.cand64, p.ev.red));
     return;
   }
   const int L = ctx[b];
@@ -726,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
     scan_unit<T, D, U>(sh, q, 1, summ + ((size_t)unit * sh.NBmax + c0) * 2 * D, b, h, len, p.keys);
     __syncthreads();
     return topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key, p.cand_idx,
-                                            p.cand_key, p.ev.red);
+                                            p.cand64, p.ev.red);
   };
   if (!whole) {
     __shared__ int last;

@@ -198,36 +198,45 @@ constexpr int kMaxKpt = 32;
 // Scratch `red` (LDS ints): [2][kWaves][4] counts (eviction; the top-K
 // exchanges its per-wave OR reductions there), four spare ints,
 // [2][kMaxKpt][kWaves] top-K compaction counts (then its partial ranks), then
-// three 256-bin radix histograms.
+// four 256-bin radix histograms (one per round), the round-0 digits' bucket
+// fill counters and bucket offsets.
 constexpr int kRedHist = 2 * kWaves * 4 + 4 + 2 * kMaxKpt * kWaves;
-constexpr int kRedInts = kRedHist + 3 * 256;
+constexpr int kRedInts = kRedHist + 6 * 256;
 
 // Selects the min(K, nb) best keys; writes sel_idx[0..kk) / sel_key[0..kk) in
-// (key desc, index asc) order and returns kk.  cand_* are (K + 4)-entry
-// scratch.  Requires nb <= KPT * kThreads.  Thread t holds keys t, t + kThreads,
-// ... in registers for the whole selection.
+// (key desc, index asc) order and returns kk.  cand_idx / cand64 are
+// (K + 4)-entry scratch.  Requires nb <= KPT * kThreads.  Thread t holds keys
+// t, t + kThreads, ... in registers for the whole selection.
 //
 // 1. The K-th largest key T: the bits all keys share are found first (wave
 //    OR reductions of the keys and of their complements); then radix
 //    selection eight bits at a time from the highest differing bit: the keys
 //    that match the digits chosen so far are counted per next digit in an
-//    LDS histogram (one barrier per round) and every wave finds, on its own,
-//    the digit at which the count of larger keys reaches kk (a DPP prefix sum
-//    over 4 digits per lane).  Three histograms rotate so that clearing one
-//    never races with the use of another.  When the chosen digit's count
-//    equals the number still needed, every key at or above the prefix is
-//    selected and the search stops early with no ties.  Key 0 is never a
-//    score key (score_key maps every finite score above it) and marks the
-//    padding.
-// 2. Compaction in index order (chunk, wave, lane), from one packed
-//    (above, tied) count per chunk and wave: keys above T go to cand_*, the
-//    lowest-index ties straight to the end of the sorted list.
-// 3. Ranking of the keys above T by (key desc, position asc).
+//    LDS histogram (one barrier per round; the four histograms are cleared
+//    up front) and every wave finds, on its own, the digit at which the count
+//    of larger keys reaches kk (a DPP prefix sum over 4 digits per lane).
+//    When the chosen digit's count equals the number still needed, every key
+//    at or above the prefix is selected and the search stops early with no
+//    ties.  Key 0 is never a score key (score_key maps every finite score
+//    above it) and marks the padding.
+// 2. No ties (the usual case): the kk selected keys are bucketed by their
+//    round-0 digit (each bucket's offset is the count of keys in higher
+//    digits, from that round's prefix sums; a slot inside the bucket from an
+//    LDS counter) and each is ranked only against its own bucket by the
+//    packed (key, ~index), so that an entry compares against a few others
+//    instead of all kk.
+// 3. Ties at T: compaction in index order (chunk, wave, lane) from one packed
+//    (above, tied) count per chunk and wave: keys above T go to the
+//    candidates, the lowest-index ties straight to the end of the sorted
+//    list; then every candidate is ranked against all of them (2-4 threads
+//    per candidate, each over a part of the list) by the packed
+//    (key, ~index).
 template <int KPT>
 __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, int* sel_idx,
-                                         uint32_t* sel_key, int* cand_idx, uint32_t* cand_key,
+                                         uint32_t* sel_key, int* cand_idx, uint64_t* cand64,
                                          int* red) {
   static_assert(KPT >= 1 && KPT <= kMaxKpt, "keys per thread");
+  static_assert(kThreads == 256, "one int4 of histogram per thread to clear");
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -243,9 +252,12 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     if (k[i] != 0u) { kor |= k[i]; knand |= ~k[i]; }
   }
   // the bits every key shares need no radix round
-  int* hist = red + kRedHist;
+  int* hist = red + kRedHist;                          // [4][256]
+  int* fill = hist + 4 * 256;                          // [256]
+  int* boff = fill + 256;                              // [256]
   int* xw = red;                                       // [2][kWaves]: the eviction's counters
-  for (int e = tid; e < 2 * 256; e += kThreads) hist[e] = 0;
+  reinterpret_cast<int4*>(hist)[tid] = int4{0, 0, 0, 0};
+  fill[tid] = 0;
   {
     const uint32_t o = wave_or(kor), n = wave_or(knand);
     if (lane == 0) { xw[w] = (int)o; xw[kWaves + w] = (int)n; }
@@ -264,7 +276,7 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
   for (int r = 0; r < 4; ++r) {
     const int shift = hb - 7 - 8 * r;                  // digit bits shift+7 .. shift (may be < 0)
     if (shift + 7 < 0) break;
-    int* hbuf = hist + (r % 3) * 256;
+    int* hbuf = hist + r * 256;
     const uint32_t dm = shift >= 0 ? (255u << shift) : (255u >> -shift);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -280,6 +292,11 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     const int sum = ca + cb + cc + cd;
     const int incl = wave_incl_sum(sum);
     const int excl = incl - sum;
+    // round 0: each digit's bucket offset (keys in higher digits); every wave
+    // writes the same values, so no barrier is needed before its own reads
+    if (r == 0)
+      *reinterpret_cast<int4*>(boff + 252 - 4 * lane) =
+          int4{excl + ca + cb + cc, excl + ca + cb, excl + ca, excl};
     const uint64_t cross = ballot(excl < rem && incl >= rem);
     const int L = __builtin_ctzll(cross);
     int above = excl, q = 0, cq = ca;
@@ -297,23 +314,58 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
     const int cnt = __builtin_amdgcn_readlane(cq, L);
     T |= shift >= 0 ? digit << shift : digit >> -shift;
     mask |= dm;
-    for (int e = tid; e < 256; e += kThreads) hist[((r + 2) % 3) * 256 + e] = 0;
     if (cnt == rem) {            // every key with this prefix is selected
       ge = true;
       break;
     }
   }
-  // compaction
+  if (ge) {
+    // 2. the kk keys >= T, bucketed by round-0 digit, ranked inside their bucket
+    const int shift0 = hb - 7;
+    auto digit0 = [&](uint32_t x) -> int {
+      return (int)(shift0 >= 0 ? (x >> shift0) & 255u : (x << -shift0) & 255u);
+    };
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      if (i < act && k[i] >= T && k[i] != 0u) {
+        const int j = i * kThreads + tid;
+        const int d = digit0(k[i]);
+        const int pos = boff[d] + atomicAdd(&fill[d], 1);
+        cand_idx[pos] = j;
+        cand64[pos] = ((uint64_t)k[i] << 32) | (uint32_t)~j;
+      }
+    }
+    if (tid == 0) cand64[kk] = 0ull;             // pads a pair read; never ranks above
+    __syncthreads();
+    if (tid < kk) {
+      const uint64_t v = cand64[tid];
+      const uint32_t key = (uint32_t)(v >> 32);
+      const int d = digit0(key);
+      const int b0 = boff[d];
+      const int b1 = min(b0 + hist[d], kk);           // the bucket (round 0's counts)
+      int rank = b0;
+      // pairs of entries; the entries of the pair outside [b0, b1) are skipped
+      for (int p = b0 >> 1; 2 * p < b1; ++p) {
+        const u32x4 x = reinterpret_cast<const u32x4*>(cand64)[p];
+        const uint64_t a0 = ((uint64_t)x[1] << 32) | x[0];
+        const uint64_t a1 = ((uint64_t)x[3] << 32) | x[2];
+        rank += (2 * p >= b0 && a0 > v) + (2 * p + 1 < b1 && a1 > v);
+      }
+      sel_idx[rank] = cand_idx[tid];
+      sel_key[rank] = key;
+    }
+    __syncthreads();
+    return kk;
+  }
+  // 3. ties at T: ordered compaction
   int* cnt = red + 2 * kWaves * 4 + 4;
   uint64_t mgv[KPT], mev[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     mgv[i] = 0; mev[i] = 0;
     if (i < act) {
-      const bool gt = ge ? (k[i] >= T && k[i] != 0u) : k[i] > T;
-      const bool eq = !ge && k[i] == T;
-      mgv[i] = ballot(gt);
-      mev[i] = ballot(eq);
+      mgv[i] = ballot(k[i] > T);
+      mev[i] = ballot(k[i] == T);
     }
   }
 #pragma unroll
@@ -342,7 +394,7 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
       if ((mgv[i] >> lane) & 1ull) {
         const int pos = (o & 0xFFFF) + lanes_below(mgv[i]);
         cand_idx[pos] = j;
-        cand_key[pos] = k[i];
+        cand64[pos] = ((uint64_t)k[i] << 32) | (uint32_t)~j;
       }
       if ((mev[i] >> lane) & 1ull) {
         const int rr = (o >> 16) + lanes_below(mev[i]);
@@ -353,44 +405,25 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
       }
     }
   }
-  if (tid < 3) cand_key[ngt + tid] = 0u;     // padding never ranks above a key
+  if (tid == 0) cand64[ngt] = 0ull;            // padding never ranks above a key
   __syncthreads();
-  // rank the ngt keys above the threshold by (key desc, position asc).  P
-  // parts of kThreads / P threads (whole waves) each count over 1/P of the
-  // list; a wave's loop bounds are uniform: positions before all of its
-  // candidates count keys >= key, positions after all of them keys > key,
-  // and only the chunks in between need both tests.
+  // rank the ngt keys above the threshold: P parts of kThreads / P threads
+  // (whole waves), each over 1/P of the list, partial counts summed in LDS
   constexpr int kLogThreads = __builtin_ctz(kThreads);
-  const int n4 = (ngt + 3) >> 2;
   const int lp = ngt <= kThreads / 4 ? 2 : (ngt <= kThreads / 2 ? 1 : 0);   // log2 of the parts
   const int P = 1 << lp;
   const int span = kThreads >> lp;
   const int c = tid & (span - 1), part = tid >> (kLogThreads - lp);
-  const int cw0 = (w * kWave) & (span - 1);            // first candidate of the wave
-  const int pw = (w * kWave) >> (kLogThreads - lp);    // the wave's part
-  const int p0 = (pw * n4) >> lp, p1 = ((pw + 1) * n4) >> lp;
-  const int pa = min(max(p0, cw0 >> 2), p1);
-  const int pb = max(pa, min(p1, ((cw0 + kWave - 1) >> 2) + 1));
-  const uint32_t key = c < ngt ? cand_key[c] : 0u;
-  const uint32_t km = key - 1u;
+  const int n2 = (ngt + 1) >> 1;
+  const int p0 = (part * n2) >> lp, p1 = ((part + 1) * n2) >> lp;
+  const uint64_t v = c < ngt ? cand64[c] : ~0ull;
   int rank = 0;
-#pragma unroll 4
-  for (int p = p0; p < pa; ++p) {
-    const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rank += kp[e] > km;
-  }
-#pragma unroll 4
-  for (int p = pa; p < pb; ++p) {
-    const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rank += kp[e] > (4 * p + e < c ? km : key);
-  }
-#pragma unroll 4
-  for (int p = pb; p < p1; ++p) {
-    const u32x4 kp = reinterpret_cast<const u32x4*>(cand_key)[p];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rank += kp[e] > key;
+#pragma unroll 8
+  for (int p = p0; p < p1; ++p) {
+    const u32x4 x = reinterpret_cast<const u32x4*>(cand64)[p];
+    const uint64_t a0 = ((uint64_t)x[1] << 32) | x[0];
+    const uint64_t a1 = ((uint64_t)x[3] << 32) | x[2];
+    rank += (a0 > v) + (a1 > v);
   }
   if (P > 1) {
     if (part > 0 && c < ngt) cnt[(part - 1) * span + c] = rank;   // compaction counts are spent
@@ -400,7 +433,7 @@ __device__ __forceinline__ int topk_unit(const uint32_t* keys, int nb, int K, in
   }
   if (part == 0 && c < ngt) {
     sel_idx[rank] = cand_idx[c];
-    sel_key[rank] = key;
+    sel_key[rank] = (uint32_t)(v >> 32);
   }
   __syncthreads();
   return kk;
@@ -551,13 +584,13 @@ __device__ __forceinline__ void evict_unit(const int* T, int K, int NBmax, int s
 
 // LDS layout of the select phase (scan keys + top-K + eviction), in bytes.
 struct SelectLds {
-  int keys, cand_idx, cand_key, sel_idx, sel_key, p2l_s, ls_s, miss, vkey, bits, red, total;
+  int keys, cand_idx, cand64, sel_idx, sel_key, p2l_s, ls_s, miss, vkey, bits, red, total;
   __host__ __device__ SelectLds(int NBmax, int K) {
     int o = 0;
     auto take = [&](int bytes) { int r = o; o += (bytes + 15) & ~15; return r; };
     keys = take(NBmax * 4);
     cand_idx = take((K + 4) * 4);
-    cand_key = take((K + 4) * 4);
+    cand64 = take((K + 4) * 8);
     sel_idx = take(K * 4);
     sel_key = take(K * 4);
     p2l_s = take(K * 4);
