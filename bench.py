@@ -55,8 +55,7 @@ def algorithmic_bytes(cfg, ctx: np.ndarray) -> dict:
     q_out = 2 * (B * 2 * Hq * d * es)                      # queries read, outputs written
     maps = B * H * (K * 4 * 2          # p2l read + write
                     + K * 4 * 2        # last_sel read + write
-                    + K * 4            # l2p lookups of the top-K
-                    + 2 * m * 4        # l2p updates
+                    + 2 * m * 4        # l2p updates (residency comes from p2l)
                     + K * 8            # top-K index + score written
                     + K * 12 + 4)      # admission list + count written
     return dict(kv=kv, summaries=summ, q_out=q_out, maps=maps,
