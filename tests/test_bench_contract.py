@@ -26,12 +26,12 @@ def test_algorithmic_bytes_of_the_16k_layer_step():
     from sparse_kv_block_amd.configs import QWEN3_8B_16K
     algo = bench.algorithmic_bytes(QWEN3_8B_16K, gen.context_lengths(QWEN3_8B_16K))
     # resident KV + summaries + q/out + maps + context lengths, one launch; per
-    # unit the maps move p2l and stamps read and written (4 K ints), K slot
-    # lookups, 2m slot updates, K (index, score) pairs, K admission triples
-    # and their count
+    # unit the maps move p2l and stamps read and written (4 K ints), 2m slot
+    # updates, K (index, score) pairs, K admission triples and their count
+    # (residency comes from p2l: no slot lookup per top-K entry)
     K, m = 128, 6
-    maps_per_unit = 4 * K * 4 + K * 4 + 2 * m * 4 + K * 8 + K * 12 + 4
-    assert maps_per_unit == 5_172
+    maps_per_unit = 4 * K * 4 + 2 * m * 4 + K * 8 + K * 12 + 4
+    assert maps_per_unit == 4_660
     assert algo["total"] == 1_073_741_824 + 536_870_912 + 4_194_304 + 1024 * maps_per_unit + 512
     assert bench.kernel_name(QWEN3_8B_16K) == "layer_step_kernel<bf16, d=128, 1 row tile>"
 
