@@ -163,8 +163,9 @@ struct StepWorkspace {
   unsigned long long tag;        // this launch's tag (bits 16..63, odd there; bits 0..15 zero)
 };
 
-// Workgroups per unit of the fused step: one when the whole context fits one
-// scan part; otherwise one for the attention plus one per scan part.
+// Scan parts of a context (at least one), and the workgroup slots per unit of
+// a fused-step launch: one when every context fits one scan part; otherwise
+// one for the attention plus one per scan part of the longest context.
 __host__ __device__ inline int scan_parts(int nb) {
   return nb > kScanChunk ? (nb + kScanChunk - 1) / kScanChunk : 1;
 }

@@ -319,12 +319,9 @@ __device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, in
 // shortest work.  Item j (0-based) maps to (unit, scan part sp): first every
 // full kScanChunk-block part (part 0 of every unit that has one, then part 1,
 // ...), then the shorter last parts, longest first (in 128-block bands, each
-// in request order), every request's heads together.  SINGLE: units whose
-// context fits one part have a scan item too (the standalone scan); without
-// it they have none (the fused step scans them with the attention).
-// Returns false past the last item.  Every wave computes the same result:
-// one ballot per group and 64 requests, twice.
-template <bool SINGLE>
+// in request order), every request's heads together; a unit whose context
+// fits one part has one item.  Returns false past the last item.  Every wave
+// computes the same result: one ballot per group and 64 requests, twice.
 __device__ __forceinline__ bool scan_item(const Shape& sh, const int32_t* __restrict__ ctx, int j,
                                           int& unit, int& sp) {
   constexpr int kFull = kMaxBlocks / kScanChunk;       // groups of full parts
@@ -333,7 +330,7 @@ __device__ __forceinline__ bool scan_item(const Shape& sh, const int32_t* __rest
   int full = 0, band = -1, np = 0;
   auto info = [&](int bb) {
     const int nb = bb < sh.B ? n_blocks(ctx[bb], sh.NBmax) : -1;
-    np = nb < 0 ? 0 : (nb > kScanChunk ? (nb + kScanChunk - 1) / kScanChunk : (SINGLE ? 1 : 0));
+    np = nb < 0 ? 0 : (nb > kScanChunk ? (nb + kScanChunk - 1) / kScanChunk : 1);
     const int rem = np > 0 ? nb - (np - 1) * kScanChunk : 0;     // blocks of the last part
     full = rem == kScanChunk ? np : (np > 0 ? np - 1 : 0);
     band = (np > 0 && rem < kScanChunk) ? kBands - 1 - (rem > 0 ? (rem - 1) / 128 : 0) : -1;
@@ -400,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T*
   const int units = sh.B * sh.H;
   int unit = blockIdx.x % units;
   int part = blockIdx.x / units;
-  if (ordered && !scan_item<true>(sh, ctx, blockIdx.x, unit, part)) return;
+  if (ordered && !scan_item(sh, ctx, blockIdx.x, unit, part)) return;
   const int b = unit / sh.H, h = unit % sh.H;
   const int nb = n_blocks(ctx[b], sh.NBmax);
   const int np = scan_parts(nb);
@@ -631,10 +628,11 @@ __host__ __device__ constexpr int attn_region(int D, int RT) {
   return (attn_lds_bytes(D, RT) + 15) & ~15;
 }
 
-// Long contexts (more than kScanChunk blocks) split a unit over several
-// workgroups: part 0 runs the attention, part p >= 1 scans blocks
-// [(p-1)*kScanChunk, p*kScanChunk), selects its local top-K and publishes it
-// to the workspace (list slot p of the unit).  (Running the attention
+// Launches with long contexts (NBmax above kScanChunk blocks) split every
+// unit over several workgroups, short contexts included: part 0 runs the
+// attention, part p >= 1 scans blocks [(p-1)*kScanChunk, p*kScanChunk),
+// selects its local top-K and publishes it to the workspace (list slot p of
+// the unit).  (Running the attention
 // interleaved with the first part's scan, as the one-part kernel does,
 // measured slower here: the scan-only workgroups then share that kernel's
 // register budget, 2 waves per SIMD instead of 3.)  All of the unit's
@@ -662,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   int unit = blockIdx.x % units;
   const int slot = blockIdx.x / units;
   int sp = -1;                             // scan part, ordered mapping
-  if (!IL && ordered && slot >= 1 && !scan_item<false>(sh, ctx, blockIdx.x - units, unit, sp))
+  if (!IL && ordered && slot >= 1 && !scan_item(sh, ctx, blockIdx.x - units, unit, sp))
     return;
   const int b = unit / sh.H, h = unit % sh.H;
   const int tid = threadIdx.x;
@@ -701,7 +699,10 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
   }
   const int L = ctx[b];
   const int nb = n_blocks(L, sh.NBmax);
-  const int active = nb > kScanChunk ? 1 + scan_parts(nb) : 1;
+  // a split launch hands every non-empty unit to an attention workgroup and
+  // its scan parts (one for a context that fits one part): the longest item
+  // is then one attention pass, not attention and scan back to back
+  const int active = parts > 1 && nb > 0 ? 1 + scan_parts(nb) : 1;
   // Without the ordered mapping (more than kOrderedMaxBatch requests) a split
   // unit's last (shortest) scan part takes the last slot: workgroups start in
   // slot order, so the launch ends on short workgroups instead of full
