@@ -109,8 +109,9 @@ struct Raw {
 // interleaved step with two row tiles takes all of up to 16 heads (every
 // supported group) in one round trip; the other paths four at a time (the
 // raw words of 16 heads would cost the split step a wave per SIMD, and the
-// one-tile step measured slower with 8 or 16).
-template <typename T, int D, int CPL, int KB = 4>
+// one-tile step measured slower with 8 or 16).  FULL: G is a multiple of KB,
+// so no row past G needs its select.
+template <typename T, int D, int CPL, int KB = 4, bool FULL = false>
 __device__ __forceinline__ void group_query_sums(const Shape& sh, const T* __restrict__ q,
                                                  int q_row, int b, int h, int c0, float* Nq,
                                                  float* Pq) {
@@ -126,7 +127,7 @@ __device__ __forceinline__ void group_query_sums(const Shape& sh, const T* __res
     }
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const bool in = i0 + k < sh.G;    // a select, not a branch: the loads stay together
+      const bool in = FULL || i0 + k < sh.G;    // a select, not a branch: the loads stay together
       float v[CPL];
       r[k].unpack(v);
 #pragma unroll
