@@ -259,7 +259,8 @@ oasis_status oasis_topk_agreement(const oasis_shape* shape,
 
 /* Workspace bytes oasis_layer_step and oasis_score_topk need for a shape: 0
  * while max_blocks <= 1024, otherwise a few KiB per unit (the per-part top-K
- * lists of the split summary scan and one 8-byte arrival word). */
+ * lists of the split summary scan, the 1024 keys of a unit's last part, which
+ * oasis_score_topk hands over unselected, and one 8-byte arrival word). */
 size_t oasis_layer_step_workspace_bytes(const oasis_shape* shape);
 
 /* S1..S4 fused — one look-ahead layer step in one launch: attention of both

@@ -156,9 +156,9 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 constexpr int kScanChunk = 1024;   // blocks per scan part
 
 struct StepWorkspace {
-  int32_t* n;                    // [units][parts]  length of each scan part's list
-  uint32_t* key;                 // [units][parts][K]
+  uint32_t* key;                 // [units][parts][K]  a scan part's list, padded with key 0
   int32_t* idx;                  // [units][parts][K]
+  uint32_t* raw;                 // [units][kScanChunk]  the last scan part's keys, unselected
   unsigned long long* arrive;    // [units]  tagged arrival count of the fused step
   unsigned long long tag;        // this launch's tag (bits 16..63, odd there; bits 0..15 zero)
 };
@@ -177,7 +177,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 
 __host__ __device__ inline size_t step_workspace_bytes(int units, int parts, int K) {
   if (parts <= 1) return 0;
-  return align256((size_t)units * parts * 4) + 2 * align256((size_t)units * parts * K * 4) +
+  return 2 * align256((size_t)units * parts * K * 4) + align256((size_t)units * kScanChunk * 4) +
          align256((size_t)units * 8);
 }
 
@@ -185,12 +185,12 @@ __host__ __device__ inline StepWorkspace step_workspace(void* base, int units, i
   StepWorkspace w{nullptr, nullptr, nullptr, nullptr, 0};
   if (parts <= 1 || base == nullptr) return w;
   char* p = static_cast<char*>(base);
-  w.n = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)units * parts * 4);
   w.key = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)units * parts * K * 4);
   w.idx = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)units * parts * K * 4);
+  w.raw = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)units * kScanChunk * 4);
   w.arrive = reinterpret_cast<unsigned long long*>(p);
   return w;
 }

@@ -200,7 +200,8 @@ __device__ __forceinline__ V ws_load(const V* ptr) {
     return *ptr;
 }
 
-// A scan part's list (slot 1 + part of the unit): blocks c0 + local index.
+// A scan part's list (slot 1 + part of the unit), all K entries (key 0 past
+// the list's length): blocks c0 + local index.
 __device__ __forceinline__ void publish_list(const Shape& sh, const StepWorkspace& ws, int unit,
                                              int parts, int part, int c0, int kk,
                                              const SelectPtrs& p) {
@@ -209,86 +210,115 @@ __device__ __forceinline__ void publish_list(const Shape& sh, const StepWorkspac
     ws_store(&ws.key[slot * sh.K + t], t < kk ? p.sel_key[t] : 0u);
     ws_store(&ws.idx[slot * sh.K + t], t < kk ? c0 + p.sel_idx[t] : -1);
   }
-  if (threadIdx.x == 0) ws_store(&ws.n[slot], kk);
+}
+
+// The last scan part's keys, unselected (the merge selects over them).
+__device__ __forceinline__ void publish_raw(const StepWorkspace& ws, int unit, int len,
+                                            const uint32_t* keys) {
+  for (int j = threadIdx.x; j < len; j += kThreads)
+    ws_store(&ws.raw[(size_t)unit * kScanChunk + j], keys[j]);
 }
 
 // Called by every thread of each of the unit's `total` workgroups once its
 // stores to the workspace are issued; true in the last one to arrive.
+// ONLY_IF_LAST: arrive only when every other workgroup has arrived (one
+// exchange that expects exactly that word, in one round trip), else leave the
+// word as it is and return false (the caller then publishes and arrives).
+// (Starting every arrival with that exchange instead of a load measured 1 us
+// slower in the fused step.)
+template <bool ONLY_IF_LAST = false>
 __device__ __forceinline__ bool arrive_last(const StepWorkspace& ws, int unit, int total,
                                             int* flag) {
   __builtin_amdgcn_s_waitcnt(0);           // this thread's stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned long long* w = ws.arrive + unit;
-    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int c;
+    unsigned long long old =
+        ONLY_IF_LAST ? ws.tag | (unsigned)(total - 1)
+                     : __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool last = false;
     for (;;) {                             // ends: a failed exchange means another arrival
-      c = (old >> 16) == (ws.tag >> 16) ? (int)(old & 0xffffu) : 0;
-      const unsigned long long nw = c + 1 == total ? ws.tag : (ws.tag | (unsigned)(c + 1));
+      const int c = (old >> 16) == (ws.tag >> 16) ? (int)(old & 0xffffu) : 0;
+      last = c + 1 == total;
+      if (ONLY_IF_LAST && !last) break;
+      const unsigned long long nw = last ? ws.tag : (ws.tag | (unsigned)(c + 1));
       if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT))
         break;
+      if (ONLY_IF_LAST) { last = false; break; }
     }
-    *flag = c + 1 == total;
+    *flag = last;
   }
   __syncthreads();
   return *flag != 0;
 }
 
-// LDS for the concatenated lists of a merge (keys, then block indices).
+// LDS for a merge's list entries: block indices from its start, keys at its
+// end, right below the select area's key array.
 __host__ __device__ inline int merge_lds_bytes(int parts, int K) {
   return parts > 1 ? (((parts - 1) * K * 8 + 15) & ~15) : 0;
 }
 
-// The merge of a split unit's np lists (each sorted by (key desc, block asc),
-// covering ascending block ranges): concatenated in part order, so equal keys
-// stay in ascending block order and the final top-K equals that of one scan
-// over the whole context; then the list out and (EVICT) the capped eviction.
+// The merge of a split unit's scan parts (nb blocks): the lists of parts
+// 0 .. nlists-1 (each sorted by (key desc, block asc); a part's list holds
+// min(K, its blocks) entries, so only the unit's last part can have fewer
+// than K) and, RAW, the keys of part nlists, which skipped its own
+// selection, concatenated in part order, so equal keys stay in ascending
+// block order and the final top-K equals that of one scan over the whole
+// context; then the list out and (EVICT) the capped eviction.  The
+// concatenated keys end where the select area's key array begins, which
+// holds the raw part's keys: LOCAL, this workgroup scanned that part and
+// they are there already; otherwise they come from the workspace.
 // COHERENT: the lists were written in the same launch.
 template <bool EVICT, bool COHERENT>
-__device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, int step,
-                                           int max_admit, int32_t* __restrict__ topk_idx,
+__device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int nb, int nlists,
+                                           bool raw, bool local,
+                                           int step, int max_admit,
+                                           int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_score, int32_t* l2p,
                                            int32_t* p2l, int32_t* last_sel, int32_t* admit,
                                            int32_t* admit_count, int parts,
                                            const StepWorkspace& ws, const SelectPtrs& p,
                                            char* merge_lds) {
   const int tid = threadIdx.x;
-  uint32_t* mkey = reinterpret_cast<uint32_t*>(merge_lds);
-  int* midx = reinterpret_cast<int*>(mkey + (parts - 1) * sh.K);
-  // every part's length, then all entries in one pass (entries past a list's
-  // length are not stored).  (Issuing the entry loads with the lengths, in one
-  // round trip, measured slower: the registers they hold.)
-  // (EVICT: the slot map and stamps are staged with them)
-  int* lens = p.ev.red;                       // the eviction's counters are free here
+  const int lb = nb - (nlists - 1) * kScanChunk;   // blocks of the last list's part
+  const int nl = (nlists - 1) * sh.K + min(sh.K, min(lb, kScanChunk));   // list entries
+  const int total = nl + (raw ? nb - nlists * kScanChunk : 0);
+  uint32_t* mkey = p.keys - nl;
+  int* midx = reinterpret_cast<int*>(merge_lds);
+  // every entry in one round trip (EVICT: the slot map and stamps with them)
   EvictStage ev{};
   if constexpr (EVICT)
     ev = evict_load(sh.K, p2l + (size_t)unit * sh.K, last_sel + (size_t)unit * sh.K);
-  if (tid < np) {
-    const int n = ws_load<COHERENT>(&ws.n[(size_t)unit * parts + 1 + tid]);
-    lens[tid] = n < 0 ? 0 : (n > sh.K ? sh.K : n);
-  }
-  if constexpr (EVICT) evict_commit(sh.K, sh.NBmax, ev, p.ev);
-  __syncthreads();
-  int total = 0;
-  for (int pp = 0; pp < np; ++pp) total += lens[pp];
-  for (int e = tid; e < np * sh.K; e += kThreads) {
-    const int pp = e / sh.K, r = e % sh.K;
-    const size_t sl = (size_t)unit * parts + 1 + pp;
-    const uint32_t k = ws_load<COHERENT>(&ws.key[sl * sh.K + r]);
-    const int i = ws_load<COHERENT>(&ws.idx[sl * sh.K + r]);
-    int off = 0;
-    for (int x = 0; x < pp; ++x) off += lens[x];
-    if (r < lens[pp]) {
-      mkey[off + r] = k;
-      midx[off + r] = i;
+  constexpr int kMaxEntries = (kMaxBlocks / kScanChunk - 1) * 256 + kScanChunk;
+  constexpr int kPer = (kMaxEntries + kThreads - 1) / kThreads;
+  const int nload = local ? nl : total;
+  uint32_t kv[kPer];
+  int iv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid + i * kThreads;
+    kv[i] = 0u;
+    iv[i] = 0;
+    if (e < nl) {
+      const int pp = e / sh.K;
+      const size_t sl = ((size_t)unit * parts + 1 + pp) * sh.K + (e - pp * sh.K);
+      kv[i] = ws_load<COHERENT>(&ws.key[sl]);
+      iv[i] = ws_load<COHERENT>(&ws.idx[sl]);
+    } else if (e < nload) {
+      kv[i] = ws_load<COHERENT>(&ws.raw[(size_t)unit * kScanChunk + (e - nl)]);
     }
   }
+  if constexpr (EVICT) evict_commit(sh.K, sh.NBmax, ev, p.ev);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid + i * kThreads;
+    if (e < nload) mkey[e] = kv[i];
+    if (e < nl) midx[e] = iv[i];
+  }
   __syncthreads();
-  // at most kMaxBlocks / kScanChunk lists of K <= 256 entries; keys per thread
-  // sized to the unit's list total (the selection's passes run over every
-  // register slot, filled or not; the result does not depend on the count)
-  constexpr int kMergeKpt = (kMaxBlocks / kScanChunk) * 256 / kThreads;
+  // keys per thread sized to the entry count (the selection's passes run over
+  // every register slot, filled or not; the result does not depend on it)
   int kk;
   if (total <= kThreads)
     kk = topk_unit<1>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64, p.ev.red);
@@ -296,13 +326,17 @@ __device__ __forceinline__ void merge_unit(const Shape& sh, int unit, int np, in
     kk = topk_unit<2>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64, p.ev.red);
   else if (total <= 4 * kThreads)
     kk = topk_unit<4>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64, p.ev.red);
+  else if (total <= 8 * kThreads)
+    kk = topk_unit<8>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64, p.ev.red);
   else
-    kk = topk_unit<kMergeKpt>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64,
-                              p.ev.red);
+    kk = topk_unit<kPer>(mkey, total, sh.K, p.sel_idx, p.sel_key, p.cand_idx, p.cand64,
+                         p.ev.red);
   // (K <= kThreads: thread t < K owns list entry t from here on, and the
   // selection ends with a barrier)
+  const int ct = nlists * kScanChunk;               // the unselected part's first block
   for (int t = tid; t < sh.K; t += kThreads) {
-    const int i = t < kk ? midx[p.sel_idx[t]] : -1;
+    const int e = t < kk ? p.sel_idx[t] : -1;
+    const int i = e < 0 ? -1 : (e < nl ? midx[e] : ct + (e - nl));
     p.sel_idx[t] = i;
     topk_idx[(size_t)unit * sh.K + t] = i;
     topk_score[(size_t)unit * sh.K + t] = t < kk ? key_score(p.sel_key[t]) : -INFINITY;
@@ -379,12 +413,15 @@ __device__ __forceinline__ bool scan_item(const Shape& sh, const int32_t* __rest
 constexpr int kOrderedMaxBatch = 256;
 
 // Long contexts (NBmax above one scan part): workgroup (unit, part) scans the
-// part's kScanChunk blocks and selects their top-K.  A unit whose context fits
-// one part finishes here; otherwise the part's list goes to the workspace
-// (slot 1 + part of the unit, the layout of the fused step's split scan) and
-// the unit's last part to finish merges the lists.  Parts past a unit's
-// context exit at once.  (512-block parts measured the same: a faster scan,
-// a slower merge.)
+// part's kScanChunk blocks.  A unit whose context fits one part selects its
+// top-K here; otherwise every part but the last selects its local top-K and
+// publishes it to the workspace (slot 1 + part of the unit, the layout of the
+// fused step's split scan), and the last part, dispatched late in the ordered
+// map and so usually the last to finish, skips its selection: when every
+// other part has arrived it merges its keys with their lists at once, else it
+// publishes its keys unselected and the last arrival merges.  Parts past a
+// unit's context exit at once.  (512-block parts measured the same: a faster
+// scan, a slower merge.)
 template <typename T, int D, int U>
 __global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T* __restrict__ q,
                                                               int q_row, const T* __restrict__ summ,
@@ -414,12 +451,20 @@ __global__ __launch_bounds__(kThreads) void score_part_kernel(Shape sh, const T*
     select_from_keys<kScanChunk / kThreads>(sh, unit, len, topk_idx, topk_score, p);
     return;
   }
-  const int kk = topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key,
-                                                   p.cand_idx, p.cand64, p.ev.red);
-  publish_list(sh, ws, unit, parts, part, c0, kk, p);
-  if (!arrive_last(ws, unit, np, &last)) return;
-  merge_unit<false, true>(sh, unit, np, 0, 0, topk_idx, topk_score, nullptr, nullptr, nullptr,
-                          nullptr, nullptr, parts, ws, p, smem);
+  const bool tail = part == np - 1;
+  if (tail) {
+    if (!arrive_last<true>(ws, unit, np, &last)) {
+      publish_raw(ws, unit, len, p.keys);
+      if (!arrive_last(ws, unit, np, &last)) return;
+    }
+  } else {
+    const int kk = topk_unit<kScanChunk / kThreads>(p.keys, len, sh.K, p.sel_idx, p.sel_key,
+                                                     p.cand_idx, p.cand64, p.ev.red);
+    publish_list(sh, ws, unit, parts, part, c0, kk, p);
+    if (!arrive_last(ws, unit, np, &last)) return;
+  }
+  merge_unit<false, true>(sh, unit, nb, np - 1, true, tail, 0, 0, topk_idx, topk_score, nullptr,
+                          nullptr, nullptr, nullptr, nullptr, parts, ws, p, smem);
 }
 
 // ------------------------------------------------------------------ agreement diagnostic
@@ -730,6 +775,9 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
                                             p.cand64, p.ev.red);
   };
   if (!whole) {
+    // (Here every scan part selects: the last part skipping its selection, as
+    // in the standalone split scan, measured 0.5 us slower, since the
+    // attention workgroup often arrives last and then selects over its keys.)
     __shared__ int last;
     if (part == 0) {
       attention();
@@ -738,8 +786,9 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
       publish_list(sh, ws, unit, parts, part - 1, c0, kk, p);
     }
     if (!arrive_last(ws, unit, active, &last)) return;
-    merge_unit<true, true>(sh, unit, active - 1, step, max_admit, topk_idx, topk_score, l2p, p2l,
-                           last_sel, admit, admit_count, parts, ws, p, smem);
+    merge_unit<true, true>(sh, unit, nb, active - 1, false, false, step, max_admit, topk_idx,
+                           topk_score, l2p, p2l, last_sel, admit, admit_count, parts, ws, p,
+                           smem);
     return;
   }
   evict_commit(sh.K, sh.NBmax,

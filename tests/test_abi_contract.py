@@ -117,8 +117,10 @@ def test_layer_step_workspace_contract(L):
     long = shape(max_blocks=8192, k_resident=128, batch=64, n_kv_heads=8, n_q_heads=32)
     need = L.layer_step_workspace_bytes(long)
     parts, units = 1 + 8192 // 1024, 64 * 8          # attention part + 1024-block scan parts
-    assert need >= 2 * units * parts * 128 * 4
-    assert need < 5 * 2**20
+    # per unit: every part's list (keys and block indices), the last part's
+    # 1024 unselected keys and the arrival word
+    assert need >= units * (2 * parts * 128 * 4 + 1024 * 4 + 8)
+    assert need < 7 * 2**20
     p = ctypes.c_void_p(4096)
     args = [p] * 4 + [0.0, 1, 6] + [p] * 8
     assert raw.oasis_layer_step(ctypes.byref(long), *args, None, need, None) == L.ERR_INVALID
