@@ -775,9 +775,11 @@ __global__ __launch_bounds__(kThreads) void layer_step_kernel(
                                             p.cand64, p.ev.red);
   };
   if (!whole) {
-    // (Here every scan part selects: the last part skipping its selection, as
-    // in the standalone split scan, measured 0.5 us slower, since the
-    // attention workgroup often arrives last and then selects over its keys.)
+    // (Here every scan part selects.  The last part skipping its selection,
+    // as in the standalone split scan, measured 0.5-0.7 us slower: a scan
+    // part arrives last in every unit, but the launch ends on full-part scans
+    // that start when the attention workgroups drain, and the merges that
+    // take raw keys cost more.)
     __shared__ int last;
     if (part == 0) {
       attention();
