@@ -19,61 +19,59 @@
 namespace oasis {
 
 // ------------------------------------------------------------------ summaries
-// One wave per block: lane (g, n) takes channels n*D/16 .. +D/16 of tokens
-// g, g+4, g+8, g+12; the four token groups are merged with lane exchanges.
-// The records may be host-mapped memory.
+// Four blocks per wave, one per 16-lane group: lane n of a group takes
+// channels n*D/16 .. +D/16 of every token of its block, so each token's key
+// row is one contiguous access of the group and the min and max need no lane
+// exchanges.  The tokens' loads are issued together (bf16: all 16; fp32: two
+// halves of 8, for registers).  A token past the context
+// re-reads the last valid one, which leaves min and max unchanged.  The
+// records may be host-mapped memory.
+constexpr int kSummBlocks = kWaves * 4;   // blocks per workgroup
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void summarize_kernel(Shape sh, const T* __restrict__ rec,
                                                              const int32_t* __restrict__ ctx,
                                                              T* __restrict__ summ) {
   constexpr int CPL = D / 16;
+  constexpr int TB = sizeof(T) == 2 ? kBlock : kBlock / 2;    // tokens per batch of loads
   const int unit = blockIdx.y;
-  const int b = unit / sh.H;
-  const int L = ctx[b];
+  const int L = ctx[unit / sh.H];
   const int nb = n_blocks(L, sh.NBmax);
-  const int w = threadIdx.x / kWave;
-  const int j = blockIdx.x * kWaves + w;
-  if (j >= nb) return;
   const int lane = threadIdx.x % kWave;
-  const int g = lane >> 4, n = lane & 15;
-  const int c0 = n * CPL;
+  const int j = blockIdx.x * kSummBlocks + (threadIdx.x / kWave) * 4 + (lane >> 4);
+  if (j >= nb) return;
+  const int c0 = (lane & 15) * CPL;
   int nv = L - j * kBlock;
   nv = nv > kBlock ? kBlock : nv;
-  const T* blk = rec + ((size_t)unit * sh.NBmax + j) * (2 * kBlock * D);
+  const T* blk = rec + ((size_t)unit * sh.NBmax + j) * (2 * kBlock * D) + c0;
   float mn[CPL], mx[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) { mn[c] = INFINITY; mx[c] = -INFINITY; }
-  // all four loads first (a token past the context re-reads the last valid
-  // one, which leaves min and max unchanged), then the reductions
-  Raw<T, CPL> r[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = g + 4 * i;
-    r[i].load(blk + (u < nv ? u : nv - 1) * D + c0);
+  for (int t0 = 0; t0 < kBlock; t0 += TB) {
+    Raw<T, CPL> r[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int u = t0 + i;
+      r[i].load(blk + (size_t)(u < nv ? u : nv - 1) * D);
+    }
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      float v[CPL];
+      r[i].unpack(v);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) { mn[c] = fminf(mn[c], v[c]); mx[c] = fmaxf(mx[c], v[c]); }
+    }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float v[CPL];
-    r[i].unpack(v);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) { mn[c] = fminf(mn[c], v[c]); mx[c] = fmaxf(mx[c], v[c]); }
-  }
+  T* out = summ + ((size_t)unit * sh.NBmax + j) * 2 * D + c0;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    mn[c] = xrow_min(mn[c]);
-    mx[c] = xrow_max(mx[c]);
-  }
-  if (g == 0) {
-    T* out = summ + ((size_t)unit * sh.NBmax + j) * 2 * D + c0;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if constexpr (sizeof(T) == 2) {
-        out[c] = f32_to_bf16_bits(mn[c]);
-        out[D + c] = f32_to_bf16_bits(mx[c]);
-      } else {
-        out[c] = mn[c];
-        out[D + c] = mx[c];
-      }
+    if constexpr (sizeof(T) == 2) {
+      out[c] = f32_to_bf16_bits(mn[c]);
+      out[D + c] = f32_to_bf16_bits(mx[c]);
+    } else {
+      out[c] = mn[c];
+      out[D + c] = mx[c];
     }
   }
 }
@@ -917,7 +915,7 @@ unsigned long long launch_tag() {
 
 hipError_t launch_summarize(const Shape& sh, int dtype, const void* records, const int32_t* ctx,
                             void* summ, hipStream_t st) {
-  dim3 grid((sh.NBmax + kWaves - 1) / kWaves, sh.B * sh.H);
+  dim3 grid((sh.NBmax + kSummBlocks - 1) / kSummBlocks, sh.B * sh.H);
   if (dtype == 1) {
     if (sh.d == 128)
       hipLaunchKernelGGL((summarize_kernel<uint16_t, 128>), grid, dim3(kThreads), 0, st, sh,
