@@ -28,6 +28,20 @@ namespace oasis {
 // records may be host-mapped memory.
 constexpr int kSummBlocks = kWaves * 4;   // blocks per workgroup
 
+// W words to p (16- or 8-byte aligned) with nontemporal vector stores.
+template <int W, typename T>
+__device__ __forceinline__ void store_nt(T* p, const uint32_t* w) {
+  static_assert(W == 2 || W % 4 == 0, "8- or 16-byte vectors");
+  if constexpr (W == 2) {
+    __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(p));
+  } else {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i)
+      __builtin_nontemporal_store(u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]},
+                                  reinterpret_cast<u32x4*>(p) + i);
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void summarize_kernel(Shape sh, const T* __restrict__ rec,
                                                              const int32_t* __restrict__ ctx,
@@ -63,17 +77,23 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(Shape sh, const T* 
       for (int c = 0; c < CPL; ++c) { mn[c] = fminf(mn[c], v[c]); mx[c] = fmaxf(mx[c], v[c]); }
     }
   }
-  T* out = summ + ((size_t)unit * sh.NBmax + j) * 2 * D + c0;
+  // nontemporal stores: the summaries are not read again by this launch, and
+  // streaming them past the caches keeps the mixed read/write traffic faster
+  constexpr int W = CPL * (int)sizeof(T) / 4;
+  uint32_t lo[W], hi[W];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
+  for (int i = 0; i < W; ++i) {
     if constexpr (sizeof(T) == 2) {
-      out[c] = f32_to_bf16_bits(mn[c]);
-      out[D + c] = f32_to_bf16_bits(mx[c]);
+      lo[i] = f32_to_bf16_bits(mn[2 * i]) | ((uint32_t)f32_to_bf16_bits(mn[2 * i + 1]) << 16);
+      hi[i] = f32_to_bf16_bits(mx[2 * i]) | ((uint32_t)f32_to_bf16_bits(mx[2 * i + 1]) << 16);
     } else {
-      out[c] = mn[c];
-      out[D + c] = mx[c];
+      lo[i] = __float_as_uint(mn[i]);
+      hi[i] = __float_as_uint(mx[i]);
     }
   }
+  T* out = summ + ((size_t)unit * sh.NBmax + j) * 2 * D + c0;
+  store_nt<W>(out, lo);
+  store_nt<W>(out + D, hi);
 }
 
 // ------------------------------------------------------------------ attention
