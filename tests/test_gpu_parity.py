@@ -152,10 +152,13 @@ def test_topk_with_more_slots_than_blocks_and_large_context():
 @pytest.mark.parametrize("dtype,K,d", [("bf16", 1, 128), ("bf16", 37, 64), ("bf16", 128, 128),
                                        ("bf16", 256, 128), ("f32", 128, 64)])
 def test_score_topk_split_over_scan_parts_exact_on_integer_inputs(dtype, K, d):
-    # contexts past 1024 blocks: one workgroup per 1024-block part, the last
-    # of a unit's parts to finish merges the lists; contexts on and around the
-    # part boundaries, one that fits a single part (finished by its part
-    # workgroup) and an empty request
+    # contexts past 1024 blocks: one workgroup per 1024-block part; every
+    # part but the last publishes its list, the last part hands over its keys
+    # unselected (1-block last parts finish first and take that path; a
+    # 1024-block last part, dispatched late, usually merges at once), and the
+    # last to arrive merges (K = 256 over 8 parts: 2,816 entries); contexts on
+    # and around the part boundaries, one that fits a single part (finished by
+    # its part workgroup) and an empty request
     cfg = small(dtype=dtype, batch=7, k_resident=K, head_dim=d, n_q_heads=8, n_kv_heads=2,
                 planted=0)
     ctx = [16 * 1024, 16 * 1024 + 1, 16 * 2048 + 15, 16 * 5000 - 3, 700, 0, 131072]
